@@ -1,0 +1,86 @@
+"""Shared test-side helpers: tensor <-> numpy bit views and a test-side
+builder that scatters logical per-sequence K/V into the pool layout.
+
+The pool layout is the library contract: K [NB, Hkv, 16, D] and
+V [NB, Hkv, D, 16] (bf16), token p of a sequence at physical block
+block_table[p // 16], offset p % 16.
+"""
+import numpy as np
+import torch
+
+BLOCK = 16
+NAN_BITS = np.uint16(0x7FC0)
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """bf16 tensor -> uint16 numpy bit patterns (CPU copy)."""
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def from_bits(a: np.ndarray) -> torch.Tensor:
+    """uint16 numpy bit patterns -> bf16 CPU tensor."""
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+
+
+def exact_bf16_bits(values) -> np.ndarray:
+    """Bit patterns of values that must be exactly representable in bf16."""
+    f = np.asarray(values, dtype=np.float32)
+    b = f.view(np.uint32)
+    if np.any(b & np.uint32(0xFFFF)):
+        raise ValueError("value not exactly representable in bf16")
+    return (b >> np.uint32(16)).astype(np.uint16)
+
+
+def random_bf16_bits(gen: torch.Generator, shape, sigma=1.0) -> np.ndarray:
+    x = torch.randn(*shape, generator=gen) * sigma
+    return bits(x.to(torch.bfloat16))
+
+
+def scatter_to_pool(keys_bits, values_bits, block_table, num_blocks, fill=NAN_BITS):
+    """Build K/V pools from logical per-sequence K/V.
+
+    keys_bits[s] is [L_s, Hkv, D] uint16 (bf16 bits) in logical order; the
+    token at position p goes to block block_table[s][p // 16], offset p % 16.
+    Every other slot holds `fill` (NaN by default).
+    """
+    hkv, d = keys_bits[0].shape[1], keys_bits[0].shape[2]
+    kc = np.full((num_blocks, hkv, BLOCK, d), fill, dtype=np.uint16)
+    vc = np.full((num_blocks, hkv, d, BLOCK), fill, dtype=np.uint16)
+    for s, (ks, vs) in enumerate(zip(keys_bits, values_bits)):
+        for p in range(ks.shape[0]):
+            b = int(block_table[s][p // BLOCK])
+            o = p % BLOCK
+            for g in range(hkv):
+                kc[b, g, o, :] = ks[p, g]
+                vc[b, g, :, o] = vs[p, g]
+    return kc, vc
+
+
+def padded_table(rows, width=None):
+    width = width or max(len(r) for r in rows)
+    bt = np.full((len(rows), width), -1, dtype=np.int32)
+    for i, r in enumerate(rows):
+        bt[i, :len(r)] = r
+    return bt
+
+
+def bf16_tolerance_report(gpu_f64: np.ndarray, ref_f64: np.ndarray, atol=4e-3):
+    """Per-element check: |gpu - ref| <= atol, or gpu is one of the two bf16
+    neighbours of the exact value (|gpu - ref| < ulp_bf16(ref)).  Returns a
+    dict with the literal max / mean abs error, the error of the exact value
+    rounded to bf16 (the floor no bf16 output can beat), and the counts."""
+    import oracle
+    err = np.abs(gpu_f64 - ref_f64)
+    ulp = oracle.bf16_ulp(ref_f64)
+    ok_abs = err <= atol
+    ok_ulp = err < ulp
+    floor = np.abs(oracle.f64_to_bf16_f64(ref_f64) - ref_f64)
+    return {
+        "max_abs": float(err.max()) if err.size else 0.0,
+        "mean_abs": float(err.mean()) if err.size else 0.0,
+        "floor_max_abs": float(floor.max()) if floor.size else 0.0,
+        "n_fail": int(np.count_nonzero(~(ok_abs | ok_ulp))),
+        "n_ulp_only": int(np.count_nonzero(ok_ulp & ~ok_abs)),
+        "n_nonfinite": int(np.count_nonzero(~np.isfinite(gpu_f64))),
+        "n": int(err.size),
+    }

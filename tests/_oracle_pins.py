@@ -1,0 +1,405 @@
+"""Pins for the CPU oracle: each function raises AssertionError if the oracle
+disagrees with something fixed independently of it -- hand-derived golden
+cases, 50-digit brute force on tiny inputs, closed forms, invariants, and
+library routines for the bf16 conversions.
+
+The functions take no arguments so that tests/test_oracle_mutations.py can
+rerun the whole battery against deliberately broken copies of the oracle.
+"""
+import json
+import math
+import os
+
+import mpmath
+import numpy as np
+import torch
+
+import oracle
+from _helpers import (bits, exact_bf16_bits, padded_table, random_bf16_bits,
+                      scatter_to_pool)
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                      "closed_form_cases.json")
+mpmath.mp.dps = 50
+
+
+# ---------------------------------------------------------------------------
+# Golden, hand-derived cases
+# ---------------------------------------------------------------------------
+
+def _scalar(v):
+    if isinstance(v, str):
+        if v == "-inf":
+            return -math.inf
+        if v.startswith("ln"):
+            return math.log(float(v[2:]))
+    return float(v)
+
+
+def _golden_inputs(case):
+    hq, hkv, d = case["num_q_heads"], case["num_kv_heads"], case["head_dim"]
+    if case["kind"] == "prefill":
+        lens = [p + n for p, n in zip(case["prefix_lens"], case["q_lens"])]
+    elif "context_lens" in case:
+        lens = case["context_lens"]
+    else:
+        lens = [len(k) for k in case["keys"]]
+    keys, values = [], []
+    for s, L in enumerate(lens):
+        if case["keys"] == "ones":
+            k = np.ones((L, hkv, d))
+        else:
+            k = np.asarray(case["keys"][s], dtype=np.float64)
+        if case["values"] == "position_pm":
+            v = np.zeros((L, hkv, d))
+            v[:, :, 0] = np.arange(L)[:, None]
+            v[:, :, 1] = -np.arange(L)[:, None]
+        else:
+            v = np.asarray(case["values"][s], dtype=np.float64)
+        keys.append(exact_bf16_bits(k))
+        values.append(exact_bf16_bits(v))
+    bt = padded_table(case["block_table"])
+    kc, vc = scatter_to_pool(keys, values, bt, case["num_blocks"])
+    return lens, bt, kc, vc
+
+
+def pin_golden_cases():
+    with open(GOLDEN) as f:
+        cases = json.load(f)["cases"]
+    for case in cases:
+        lens, bt, kc, vc = _golden_inputs(case)
+        hq, hkv = case["num_q_heads"], case["num_kv_heads"]
+        scale = _scalar(case["scale"])
+        exp = np.asarray(case["expected"], dtype=np.float64)
+        if case["kind"] == "prefill":
+            total = sum(case["q_lens"])
+            q = exact_bf16_bits(np.ones((total, hq, case["head_dim"])))
+            cu = np.concatenate([[0], np.cumsum(case["q_lens"])]).astype(np.int32)
+            out = oracle.prefill(q, kc, vc, bt, cu, case["prefix_lens"], scale, hq, hkv)
+        else:
+            q = exact_bf16_bits(case["q"])
+            out = oracle.decode(q, kc, vc, bt, lens, scale, hq, hkv)
+        assert np.allclose(out, exp, rtol=0, atol=1e-12), (case["name"], out, exp)
+        if case["kind"] == "partials":
+            po, pl = oracle.decode_partials(q, kc, vc, bt, lens, scale, hq, hkv,
+                                            case["partition_size"], case["num_partitions"])
+            epo = np.asarray(case["expected_part_out"], dtype=np.float64)
+            epl = np.vectorize(_scalar)(np.asarray(case["expected_part_lse"], dtype=object)).astype(np.float64)
+            assert np.allclose(po, epo, rtol=0, atol=1e-12), (case["name"], po)
+            fin = np.isfinite(epl)
+            assert np.array_equal(np.isfinite(pl), fin), (case["name"], pl)
+            assert np.allclose(pl[fin], epl[fin], rtol=0, atol=1e-12), (case["name"], pl)
+            comb = oracle.combine_partials(po, pl)
+            assert np.allclose(comb, exp, rtol=0, atol=1e-12), (case["name"], comb)
+
+
+# ---------------------------------------------------------------------------
+# bf16 conversions against known bit patterns and torch's own rounding
+# ---------------------------------------------------------------------------
+
+def pin_bf16_conversions():
+    known = {0x3F80: 1.0, 0xC000: -2.0, 0x3F81: 1.0 + 2.0 ** -7, 0x0001: 2.0 ** -133,
+             0x7F80: math.inf, 0x3E00: 0.125, 0x4049: 3.140625}
+    got = oracle.bf16_bits_to_f64(np.array(list(known.keys()), dtype=np.uint16))
+    assert np.array_equal(got, np.array(list(known.values()))), got
+    # ties to even at 1: 1 + 2^-8 -> 1, 1 + 3*2^-8 -> 1 + 2^-6
+    r = oracle.f64_to_bf16_f64([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 0.0])
+    assert np.array_equal(r, [1.0, 1 + 2.0 ** -6, -1.0, 0.0]), r
+    # agrees with torch's round-to-nearest-even fp32 -> bf16 on fp32 inputs
+    g = torch.Generator().manual_seed(7)
+    x = (torch.randn(20000, generator=g) * torch.exp(torch.randn(20000, generator=g) * 4))
+    ref = x.to(torch.bfloat16).to(torch.float64).numpy()
+    mine = oracle.f64_to_bf16_f64(x.to(torch.float64).numpy())
+    assert np.array_equal(mine, ref)
+    u = oracle.bf16_ulp(np.array([1.0, 1.5, 2.0, 3.9, 0.01]))
+    assert np.array_equal(u, [2.0 ** -7, 2.0 ** -7, 2.0 ** -6, 2.0 ** -6, 2.0 ** -14]), u
+
+
+# ---------------------------------------------------------------------------
+# 50-digit brute force on tiny inputs
+# ---------------------------------------------------------------------------
+
+def _brute_attention(qv, ks, vs, scale):
+    """Softmax attention straight from the definition, in 50-digit floats,
+    without max subtraction: sum_j exp(z_j) v_j / sum_j exp(z_j)."""
+    sc = mpmath.mpf(scale)
+    ws = []
+    for k in ks:
+        z = sc * mpmath.fsum(mpmath.mpf(a) * mpmath.mpf(b) for a, b in zip(qv, k))
+        ws.append(mpmath.exp(z))
+    den = mpmath.fsum(ws)
+    if not ws:
+        return [0.0] * len(qv), -math.inf
+    out = [float(mpmath.fsum(w * mpmath.mpf(v[i]) for w, v in zip(ws, vs)) / den) for i in range(len(qv))]
+    return out, float(mpmath.log(den))
+
+
+def _tiny_paged(gen, lens, hq, hkv, d, sigma=1.0, extra_blocks=3):
+    """Logical per-sequence K/V, scattered into a pool through a random table."""
+    nblk = [(L + 15) // 16 for L in lens]
+    nb = sum(nblk) + extra_blocks
+    perm = torch.randperm(nb, generator=gen).numpy()
+    rows, off = [], 0
+    for n in nblk:
+        rows.append(list(perm[off:off + n]))
+        off += n
+    bt = padded_table(rows, max(nblk) + 1)
+    keys = [random_bf16_bits(gen, (L, hkv, d), sigma) for L in lens]
+    values = [random_bf16_bits(gen, (L, hkv, d), sigma) for L in lens]
+    kc, vc = scatter_to_pool(keys, values, bt, nb)
+    f = oracle.bf16_bits_to_f64
+    return bt, kc, vc, [f(k) for k in keys], [f(v) for v in values]
+
+
+SHAPES = [(1, 1, 3), (2, 1, 8), (4, 2, 5), (8, 2, 4), (4, 4, 1)]
+
+
+def pin_brute_decode():
+    gen = torch.Generator().manual_seed(1234)
+    for hq, hkv, d in SHAPES:
+        lens = [1, 16, 17, 40]
+        bt, kc, vc, K, V = _tiny_paged(gen, lens, hq, hkv, d)
+        q = random_bf16_bits(gen, (len(lens), hq, d))
+        qf = oracle.bf16_bits_to_f64(q)
+        scale = 1.0 / math.sqrt(d) * 1.7
+        out = oracle.decode(q, kc, vc, bt, lens, scale, hq, hkv)
+        G = hq // hkv
+        for s, L in enumerate(lens):
+            for h in range(hq):
+                g = h // G
+                want, _ = _brute_attention(qf[s, h], K[s][:, g], V[s][:, g], scale)
+                assert np.allclose(out[s, h], want, rtol=1e-12, atol=1e-13), (hq, hkv, d, s, h)
+
+
+def pin_brute_prefill():
+    gen = torch.Generator().manual_seed(99)
+    for hq, hkv, d in SHAPES[:4]:
+        q_lens, prefix = [5, 1, 18], [0, 17, 3]
+        lens = [n + p for n, p in zip(q_lens, prefix)]
+        bt, kc, vc, K, V = _tiny_paged(gen, lens, hq, hkv, d)
+        total = sum(q_lens)
+        q = random_bf16_bits(gen, (total, hq, d))
+        qf = oracle.bf16_bits_to_f64(q)
+        cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+        scale = 0.9 / math.sqrt(d)
+        out = oracle.prefill(q, kc, vc, bt, cu, prefix, scale, hq, hkv)
+        G = hq // hkv
+        for s in range(len(q_lens)):
+            for i in range(q_lens[s]):
+                row = cu[s] + i
+                n_vis = prefix[s] + i + 1
+                for h in range(hq):
+                    g = h // G
+                    want, _ = _brute_attention(qf[row, h], K[s][:n_vis, g], V[s][:n_vis, g], scale)
+                    assert np.allclose(out[row, h], want, rtol=1e-12, atol=1e-13), (s, i, h)
+
+
+def pin_brute_partials():
+    gen = torch.Generator().manual_seed(5)
+    hq, hkv, d = 4, 2, 3
+    lens = [1, 33, 47, 0]
+    bt, kc, vc, K, V = _tiny_paged(gen, [max(L, 1) for L in lens], hq, hkv, d)
+    q = random_bf16_bits(gen, (len(lens), hq, d))
+    qf = oracle.bf16_bits_to_f64(q)
+    ps, P = 16, 4
+    po, pl = oracle.decode_partials(q, kc, vc, bt, lens, 0.5, hq, hkv, ps, P)
+    for s, L in enumerate(lens):
+        for h in range(hq):
+            g = h // (hq // hkv)
+            for p in range(P):
+                lo, hi = p * ps, min(L, (p + 1) * ps)
+                want, lse = _brute_attention(qf[s, h], K[s][lo:hi, g] if hi > lo else [],
+                                             V[s][lo:hi, g] if hi > lo else [], 0.5)
+                assert np.allclose(po[s, h, p], want, rtol=1e-12, atol=1e-13), (s, h, p)
+                if hi > lo:
+                    assert abs(pl[s, h, p] - lse) < 1e-12, (s, h, p, pl[s, h, p], lse)
+                else:
+                    assert pl[s, h, p] == -math.inf
+    out = oracle.decode(q, kc, vc, bt, lens, 0.5, hq, hkv)
+    assert np.allclose(oracle.combine_partials(po, pl), out, rtol=1e-12, atol=1e-13)
+
+
+def pin_write_kv_elementwise():
+    gen = torch.Generator().manual_seed(3)
+    nb, hkv, d, T = 6, 3, 5, 9
+    kc = random_bf16_bits(gen, (nb, hkv, 16, d))
+    vc = random_bf16_bits(gen, (nb, hkv, d, 16))
+    kn = random_bf16_bits(gen, (T, hkv, d))
+    vn = random_bf16_bits(gen, (T, hkv, d))
+    slots = np.array([0, 17, 95, -1, 40, 16 * 5 + 15, 33, -7, 2], dtype=np.int64)
+    k2, v2 = oracle.write_kv(kc, vc, kn, vn, slots)
+    ek, ev = kc.copy(), vc.copy()
+    for t in range(T):
+        if slots[t] < 0:
+            continue
+        for g in range(hkv):
+            for i in range(d):
+                ek[slots[t] // 16, g, slots[t] % 16, i] = kn[t, g, i]
+                ev[slots[t] // 16, g, i, slots[t] % 16] = vn[t, g, i]
+    assert np.array_equal(k2, ek) and np.array_equal(v2, ev)
+    assert k2.dtype == np.uint16 and v2.dtype == np.uint16
+
+
+# ---------------------------------------------------------------------------
+# Closed forms
+# ---------------------------------------------------------------------------
+
+def pin_closed_forms():
+    gen = torch.Generator().manual_seed(11)
+    hq, hkv, d = 4, 2, 8
+    # single token: output is V exactly
+    bt, kc, vc, K, V = _tiny_paged(gen, [1, 1], hq, hkv, d)
+    q = random_bf16_bits(gen, (2, hq, d))
+    out = oracle.decode(q, kc, vc, bt, [1, 1], 0.3, hq, hkv)
+    for s in range(2):
+        for h in range(hq):
+            assert np.array_equal(out[s, h], V[s][0, h // 2])
+    # identical keys -> mean of V; q = 0 -> mean of V
+    lens = [23]
+    bt, kc, vc, K, V = _tiny_paged(gen, lens, hq, hkv, d)
+    kc_same = kc.copy()
+    row = kc[bt[0][0], :, 0, :].copy()
+    for p in range(23):
+        kc_same[bt[0][p // 16], :, p % 16, :] = row
+    out = oracle.decode(q[:1], kc_same, vc, bt, lens, 0.7, hq, hkv)
+    for h in range(hq):
+        assert np.allclose(out[0, h], V[0][:, h // 2].mean(axis=0), rtol=1e-13, atol=1e-14)
+    qz = np.zeros_like(q[:1])
+    out = oracle.decode(qz, kc, vc, bt, lens, 0.7, hq, hkv)
+    for h in range(hq):
+        assert np.allclose(out[0, h], V[0][:, h // 2].mean(axis=0), rtol=1e-13, atol=1e-14)
+    # two keys: sigmoid weights
+    bt, kc, vc, K, V = _tiny_paged(gen, [2], hq, hkv, d)
+    qf = oracle.bf16_bits_to_f64(q[:1])
+    out = oracle.decode(q[:1], kc, vc, bt, [2], 0.25, hq, hkv)
+    for h in range(hq):
+        g = h // 2
+        z0, z1 = 0.25 * K[0][0, g] @ qf[0, h], 0.25 * K[0][1, g] @ qf[0, h]
+        s0 = 1.0 / (1.0 + math.exp(z1 - z0))
+        s1 = 1.0 / (1.0 + math.exp(z0 - z1))
+        assert np.allclose(out[0, h], s0 * V[0][0, g] + s1 * V[0][1, g], rtol=1e-13, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Invariants
+# ---------------------------------------------------------------------------
+
+def _case_bits(case):
+    return (bits(case.q), bits(case.k_cache), bits(case.v_cache),
+            case.block_tables.numpy(), case.context_lens.numpy())
+
+
+def pin_block_permutation_and_contiguous_twin():
+    from workloads import make_decode_case
+    c = make_decode_case("inv", context_lens=[1, 15, 16, 17, 40], num_q_heads=8,
+                         num_kv_heads=2, head_dim=16, num_blocks=24, seed=21, poison=False)
+    q, kc, vc, bt, ctx = _case_bits(c)
+    base = oracle.decode(q, kc, vc, bt, ctx, c.scale, 8, 2)
+    gen = torch.Generator().manual_seed(8)
+    perm = torch.randperm(24, generator=gen).numpy()
+    kc2, vc2 = np.empty_like(kc), np.empty_like(vc)
+    kc2[perm] = kc
+    vc2[perm] = vc
+    bt2 = np.where(bt >= 0, perm[np.maximum(bt, 0)], -1).astype(np.int32)
+    assert np.array_equal(oracle.decode(q, kc2, vc2, bt2, ctx, c.scale, 8, 2), base)
+    # contiguous twin: blocks laid out in logical order behind an identity-like table
+    rows, nxt = [], 0
+    kc3, vc3 = np.zeros_like(kc), np.zeros_like(vc)
+    for s in range(len(ctx)):
+        nb = (int(ctx[s]) + 15) // 16
+        rows.append(list(range(nxt, nxt + nb)))
+        for j in range(nb):
+            kc3[nxt + j] = kc[bt[s, j]]
+            vc3[nxt + j] = vc[bt[s, j]]
+        nxt += nb
+    bt3 = padded_table(rows, bt.shape[1])
+    assert np.array_equal(oracle.decode(q, kc3, vc3, bt3, ctx, c.scale, 8, 2), base)
+
+
+def pin_poison_ignored():
+    from workloads import make_decode_case
+    a = make_decode_case("p", context_lens=[3, 20, 33], num_q_heads=4, num_kv_heads=2,
+                         head_dim=8, num_blocks=10, seed=4, poison=False)
+    b = make_decode_case("p", context_lens=[3, 20, 33], num_q_heads=4, num_kv_heads=2,
+                         head_dim=8, num_blocks=10, seed=4, poison=True)
+    # make b's live slots identical to a's (poisoning covers the decoded
+    # token's slot too; restore it)
+    kb, vb = bits(b.k_cache), bits(b.v_cache)
+    ka, va = bits(a.k_cache), bits(a.v_cache)
+    kb, vb = oracle.write_kv(kb, vb, np.stack([ka[s // 16, :, s % 16, :] for s in a.slot_mapping.numpy()]),
+                             np.stack([va[s // 16, :, :, s % 16] for s in a.slot_mapping.numpy()]),
+                             a.slot_mapping.numpy())
+    assert np.isnan(oracle.bf16_bits_to_f64(kb)).any()
+    q, ctx, bt = bits(a.q), a.context_lens.numpy(), a.block_tables.numpy()
+    ra = oracle.decode(q, ka, va, bt, ctx, a.scale, 4, 2)
+    rb = oracle.decode(q, kb, vb, bt, ctx, a.scale, 4, 2)
+    assert np.isfinite(rb).all() and np.array_equal(ra, rb)
+
+
+def pin_causal_perturbation_and_prefill_vs_decode():
+    from workloads import make_prefill_case
+    c = make_prefill_case("c", q_lens=[7, 20], prefix_lens=[0, 18], num_q_heads=4,
+                          num_kv_heads=2, head_dim=8, num_blocks=12, seed=17, poison=False)
+    kc, vc = oracle.write_kv(bits(c.k_cache), bits(c.v_cache), bits(c.k_new), bits(c.v_new),
+                             c.slot_mapping.numpy())
+    q, bt = bits(c.q), c.block_tables.numpy()
+    cu, pl = c.cu_seqlens.numpy(), c.prefix_lens.numpy()
+    base = oracle.prefill(q, kc, vc, bt, cu, pl, c.scale, 4, 2)
+    # each row equals a decode of that token over context prefix+i+1
+    for s in range(2):
+        for i in range(c.q_lens[s]):
+            row = cu[s] + i
+            dec = oracle.decode(q[row:row + 1], kc, vc, bt[s:s + 1], [pl[s] + i + 1], c.scale, 4, 2)
+            assert np.allclose(base[row], dec[0], rtol=1e-13, atol=1e-14), (s, i)
+    # perturbing K/V of positions after prefix+i leaves rows <= i unchanged
+    s, i = 1, 9
+    kc2, vc2 = kc.copy(), vc.copy()
+    for p in range(pl[s] + i + 1, pl[s] + c.q_lens[s]):
+        b, o = bt[s, p // 16], p % 16
+        kc2[b, :, o, :] ^= np.uint16(0x0040)
+        vc2[b, :, :, o] ^= np.uint16(0x0040)
+    pert = oracle.prefill(q, kc2, vc2, bt, cu, pl, c.scale, 4, 2)
+    rows = slice(cu[s], cu[s] + i + 1)
+    assert np.array_equal(pert[rows], base[rows])
+    assert not np.allclose(pert[cu[s] + i + 1], base[cu[s] + i + 1])
+
+
+def pin_gqa_equals_repeated_mha():
+    from workloads import make_decode_case
+    hq, hkv, d = 8, 2, 8
+    c = make_decode_case("g", context_lens=[5, 31], num_q_heads=hq, num_kv_heads=hkv,
+                         head_dim=d, num_blocks=6, seed=23, poison=False)
+    q, kc, vc, bt, ctx = _case_bits(c)
+    gqa = oracle.decode(q, kc, vc, bt, ctx, c.scale, hq, hkv)
+    G = hq // hkv
+    kc_m = np.repeat(kc, G, axis=1)     # KV head h' = h // G
+    vc_m = np.repeat(vc, G, axis=1)
+    mha = oracle.decode(q, kc_m, vc_m, bt, ctx, c.scale, hq, hq)
+    assert np.array_equal(gqa, mha)
+
+
+def pin_partials_combine_equals_unsplit():
+    from workloads import make_decode_case
+    c = make_decode_case("s", context_lens=[1, 64, 100, 257], num_q_heads=4, num_kv_heads=1,
+                         head_dim=8, num_blocks=30, seed=31, poison=False)
+    q, kc, vc, bt, ctx = _case_bits(c)
+    full = oracle.decode(q, kc, vc, bt, ctx, c.scale, 4, 1)
+    for ps, P in [(16, 17), (64, 5), (256, 2), (512, 1)]:
+        po, pl = oracle.decode_partials(q, kc, vc, bt, ctx, c.scale, 4, 1, ps, P)
+        assert np.allclose(oracle.combine_partials(po, pl), full, rtol=1e-12, atol=1e-14), ps
+
+
+ALL_PINS = [
+    pin_golden_cases,
+    pin_bf16_conversions,
+    pin_brute_decode,
+    pin_brute_prefill,
+    pin_brute_partials,
+    pin_write_kv_elementwise,
+    pin_closed_forms,
+    pin_block_permutation_and_contiguous_twin,
+    pin_poison_ignored,
+    pin_causal_perturbation_and_prefill_vs_decode,
+    pin_gqa_equals_repeated_mha,
+    pin_partials_combine_equals_unsplit,
+]

@@ -1,0 +1,66 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and check that
+the pin battery catches each one: a wrong head mapping, index, sign, missing
+term, transposed operand or wrong rounding must fail at least one pin."""
+import os
+import types
+
+import pytest
+
+import _oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "paged_attention.py")
+
+MUTATIONS = {
+    "interleaved_kv_heads": ("return h // (num_q_heads // num_kv_heads)",
+                             "return h % num_kv_heads"),
+    "offset_off_by_one": ("return int(block_table_row[pos // BLOCK]), pos % BLOCK",
+                          "return int(block_table_row[pos // BLOCK]), (pos + 1) % BLOCK"),
+    "k_reversed_dims": ("return k_cache[block, :, off, :]",
+                        "return k_cache[block, :, off, ::-1]"),
+    "v_reversed_dims": ("return v_cache[block, :, :, off]",
+                        "return v_cache[block, :, :, off][:, ::-1]"),
+    "slot_block_offset_swapped": ("return slot // BLOCK, slot % BLOCK",
+                                  "return slot % BLOCK, slot // BLOCK"),
+    "scale_dropped": ("return scale * (q_rows_h @ K_g.T)", "return (q_rows_h @ K_g.T)"),
+    "score_sign": ("return scale * (q_rows_h @ K_g.T)", "return -scale * (q_rows_h @ K_g.T)"),
+    "softmax_sign": ("e = np.exp(z - m)\n    s = np.sum", "e = np.exp(m - z)\n    s = np.sum"),
+    "diagonal_excluded": ("return prefix_len + np.arange(n_new) + 1",
+                          "return prefix_len + np.arange(n_new)"),
+    "prefix_ignored_in_mask": ("return prefix_len + np.arange(n_new) + 1",
+                               "return np.arange(n_new) + 1"),
+    "lse_missing_max": ("part_lse[s, h, p] = m + np.log(np.sum(e))",
+                        "part_lse[s, h, p] = np.log(np.sum(e))"),
+    "combine_weight_sign": ("w = np.exp(lse - M)", "w = np.exp(M - lse)"),
+    "bf16_widen_shift": ("<< np.uint32(16)", "<< np.uint32(15)"),
+    "write_k_from_v": ("kc[b, :, o, :] = k_new[t]", "kc[b, :, o, :] = v_new[t]"),
+    "decode_excludes_self": ("np.array([n]),", "np.array([n - 1]),"),
+    "partitions_overlap": ("lo, hi = p * partition_size, min(n, (p + 1) * partition_size)",
+                           "lo, hi = p * partition_size, min(n, (p + 1) * partition_size + 1)"),
+    "prefill_prefix_not_gathered": ("gather_sequence(k_cache, v_cache, block_tables[s], P + N)",
+                                    "gather_sequence(k_cache, v_cache, block_tables[s], N)"),
+    "bf16_round_truncates": ("np.rint(np.ldexp(m, 8))", "np.trunc(np.ldexp(m, 8))"),
+}
+
+
+def _mutant(old, new):
+    with open(SRC) as f:
+        src = f.read()
+    assert src.count(old) == 1, f"mutation anchor not unique/present: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), SRC + " (mutant)", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    mod = _mutant(*MUTATIONS[name])
+    monkeypatch.setattr(pins, "oracle", mod)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin()
+        except Exception as e:  # AssertionError or a shape/index error
+            caught.append((pin.__name__, type(e).__name__))
+            break
+    assert caught, f"mutation {name} survived every oracle pin"
