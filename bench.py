@@ -1,0 +1,308 @@
+"""Benchmark: paged GQA decode KV GB/s (and prefill TFLOP/s) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers 36]
+
+One step is one decode step of a Qwen3-4B-shaped attention stack (32 query
+heads, 8 KV heads, head_dim 128, 36 layers; "Qwen3-4B / 8B / 32B", section
+Architecture Notes): for every layer, the 8 new tokens' K/V are appended
+(pa_write_kv), then split-K decode (pa_decode) and its log-sum-exp reduce
+(pa_decode_reduce) run over contexts of 1024-1152 tokens scattered over a
+4096-block pool.  Every layer has its own pools, so a step streams
+36 x ~35.7 MB of KV -- far more than the 256 MB Infinity Cache -- straight
+from HBM, as a real decode step does.  The prefill section times the
+prefill path (pa_write_kv of 4 x 1024 new tokens + pa_prefill, two of the
+sequences after 512 cached tokens) over the same 36-layer stack.
+
+Prints ONE JSON line.  `value` = whole-step KV bytes / step time.  The
+roofline object covers the decode kernel: algorithmic KV bytes per launch /
+its average launch duration measured with HIP events on the launch stream.
+cpu_baseline = the CPU fp64 oracle timed on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "paged GQA decode KV GB/s (% of HBM peak); prefill TFLOP/s (% of MFMA peak)"
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=36)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "paged_kv_gqa_write_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_file, sources):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", kernel_file)
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != source_hash(*sources):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU component)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_gqa_write_amd as pa
+    import workloads
+
+    pa.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = args.layers
+
+    # ---------------- decode: Qwen3-4B shape, batch 8 ------------------------
+    case = workloads.qwen3_4b_decode(poison=False)
+    B, hq, hkv, d = case.batch, case.num_q_heads, case.num_kv_heads, case.head_dim
+    nb = case.num_blocks
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(42)
+    kc = [case.k_cache.to(dev)]
+    vc = [case.v_cache.to(dev)]
+    for _ in range(1, L):
+        kc.append(torch.randn(kc[0].shape, generator=gen, device=dev).to(torch.bfloat16))
+        vc.append(torch.randn(vc[0].shape, generator=gen, device=dev).to(torch.bfloat16))
+    q = case.q.to(dev)
+    k_new, v_new = case.k_new.to(dev), case.v_new.to(dev)
+    slots = case.slot_mapping.to(dev)
+    bt = case.block_tables.to(dev)
+    ctx = case.context_lens.to(dev)
+    max_ctx = int(case.context_lens.max())
+    ps, npart = pa.decode_split_plan(B, hkv, max_ctx)
+    out = torch.empty(B, hq, d, dtype=torch.bfloat16, device=dev)
+    part_out = torch.empty(B, hq, npart, d, dtype=torch.float32, device=dev)
+    part_lse = torch.empty(B, hq, npart, dtype=torch.float32, device=dev)
+    lib = pa.load_library()
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+
+    def decode_layer(i):
+        st = lib.pa_write_kv(k_new.data_ptr(), v_new.data_ptr(), slots.data_ptr(),
+                             kc[i].data_ptr(), vc[i].data_ptr(), B, hkv, d, 16, nb, sptr)
+        st |= lib.pa_decode(out.data_ptr(), part_out.data_ptr(), part_lse.data_ptr(),
+                            q.data_ptr(), kc[i].data_ptr(), vc[i].data_ptr(), bt.data_ptr(),
+                            ctx.data_ptr(), B, hq, hkv, d, 16, nb, bt.shape[1], ps, npart,
+                            case.scale, sptr)
+        if npart > 1:
+            st |= lib.pa_decode_reduce(out.data_ptr(), part_out.data_ptr(), part_lse.data_ptr(),
+                                       ctx.data_ptr(), B, hq, d, ps, npart, sptr)
+        return st
+
+    def decode_step():
+        for i in range(L):
+            if decode_layer(i) != 0:
+                raise RuntimeError("decode step launch failed")
+
+    for _ in range(args.warmup):
+        decode_step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        decode_step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    kv_bytes_layer = case.kv_bytes()
+    value = kv_bytes_layer * L / (ms_step * 1e-3) / 1e9
+
+    # Decode kernel alone: HIP events around every pa_decode launch over the
+    # same K steps (pa_write_kv and the reduce run outside the brackets).
+    evs = []
+    for _ in range(args.steps):
+        for i in range(L):
+            lib.pa_write_kv(k_new.data_ptr(), v_new.data_ptr(), slots.data_ptr(),
+                            kc[i].data_ptr(), vc[i].data_ptr(), B, hkv, d, 16, nb, sptr)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            lib.pa_decode(out.data_ptr(), part_out.data_ptr(), part_lse.data_ptr(), q.data_ptr(),
+                          kc[i].data_ptr(), vc[i].data_ptr(), bt.data_ptr(), ctx.data_ptr(), B,
+                          hq, hkv, d, 16, nb, bt.shape[1], ps, npart, case.scale, sptr)
+            b.record(stream)
+            evs.append((a, b))
+            if npart > 1:
+                lib.pa_decode_reduce(out.data_ptr(), part_out.data_ptr(), part_lse.data_ptr(),
+                                     ctx.data_ptr(), B, hq, d, ps, npart, sptr)
+    torch.cuda.synchronize()
+    dec_us = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e3
+    dec_gbps = kv_bytes_layer / (dec_us * 1e-6) / 1e9
+    traffic = measured_traffic("decode_kernel_traffic.json", ["decode.hip", "pa_device.h"])
+    roofline = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                "traffic": traffic, "kernel": "decode_kernel<128>",
+                "algorithmic_bytes_per_launch": kv_bytes_layer,
+                "avg_launch_us": round(dec_us, 3)}
+
+    # plain copy bandwidth of this device, for reference
+    src = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * src.numel() * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    roofline["copy_GBps_measured"] = round(copy_gbps, 1)
+    del src, dst
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 tensors shaped like the pages' workloads)",
+        "config": {"workload": "qwen3_4b_decode_b8: one decode step of a 36-layer Qwen3-4B "
+                               "attention stack (write_kv + split-K decode + reduce per layer)",
+                   "layers": L, "batch": B, "num_q_heads": hq, "num_kv_heads": hkv,
+                   "head_dim": d, "block_size": 16, "context_lens": case.context_lens.tolist(),
+                   "num_blocks_per_layer": nb, "partition_size": ps, "num_partitions": npart},
+        "roofline": roofline,
+    }
+
+    # ---------------- prefill: Qwen3-4B shape, 4 x 1024 ----------------------
+    if not args.no_prefill:
+        del kc, vc
+        torch.cuda.empty_cache()
+        pc = workloads.qwen3_4b_prefill(poison=False)
+        pkc = [pc.k_cache.to(dev)]
+        pvc = [pc.v_cache.to(dev)]
+        for _ in range(1, L):
+            pkc.append(torch.randn(pkc[0].shape, generator=gen, device=dev).to(torch.bfloat16))
+            pvc.append(torch.randn(pvc[0].shape, generator=gen, device=dev).to(torch.bfloat16))
+        pq = pc.q.to(dev)
+        pkn, pvn = pc.k_new.to(dev), pc.v_new.to(dev)
+        pslots = pc.slot_mapping.to(dev)
+        pbt = pc.block_tables.to(dev)
+        pcu = pc.cu_seqlens.to(dev)
+        ppre = pc.prefix_lens.to(dev)
+        pout = torch.empty_like(pq)
+        T, phq, phkv, pd = pc.total_q, pc.num_q_heads, pc.num_kv_heads, pc.head_dim
+        maxq = max(pc.q_lens)
+
+        def prefill_layer(i, evpair=None):
+            st = lib.pa_write_kv(pkn.data_ptr(), pvn.data_ptr(), pslots.data_ptr(),
+                                 pkc[i].data_ptr(), pvc[i].data_ptr(), T, phkv, pd, 16,
+                                 pc.num_blocks, sptr)
+            if evpair is not None:
+                evpair[0].record(stream)
+            st |= lib.pa_prefill(pout.data_ptr(), pq.data_ptr(), pkc[i].data_ptr(),
+                                 pvc[i].data_ptr(), pbt.data_ptr(), pcu.data_ptr(),
+                                 ppre.data_ptr(), pc.num_seqs, T, maxq, phq, phkv, pd, 16,
+                                 pc.num_blocks, pbt.shape[1], pc.scale, sptr)
+            if evpair is not None:
+                evpair[1].record(stream)
+            if st != 0:
+                raise RuntimeError("prefill launch failed")
+
+        for _ in range(args.warmup):
+            for i in range(L):
+                prefill_layer(i)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(args.steps):
+            for i in range(L):
+                prefill_layer(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        pms = t0.elapsed_time(t1) / args.steps
+        flops = pc.flops()
+        pevs = []
+        for _ in range(args.steps):
+            for i in range(L):
+                pair = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                prefill_layer(i, pair)
+                pevs.append(pair)
+        torch.cuda.synchronize()
+        pf_us = sum(a.elapsed_time(b) for a, b in pevs) / len(pevs) * 1e3
+        pf_tflops = flops / (pf_us * 1e-6) / 1e12
+        result["prefill"] = {
+            "workload": "qwen3_4b_prefill_4x1024: 4 x 1024 new tokens, sequences 1 and 3 after "
+                        "512 cached tokens, 32/8 heads, head_dim 128, 36 layers "
+                        "(write_kv + prefill per layer)",
+            "value": round(flops * L / (pms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(pms, 4), "algorithmic_flops_per_layer": flops,
+            "roofline": {"bound": "mfma", "achieved": round(pf_tflops, 2),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(pf_tflops / BF16_PEAK_TFLOPS, 4),
+                         "traffic": measured_traffic("prefill_kernel_traffic.json",
+                                                     ["prefill.hip", "pa_device.h"]),
+                         "kernel": "prefill_kernel<128>", "avg_launch_us": round(pf_us, 3)},
+        }
+        del pkc, pvc
+
+    # ---------------- CPU baseline: the oracle on a bounded sample -----------
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(seconds):
+    """The fp64 oracle (as it stands) decoding the same Qwen3-4B batch-8 layer
+    repeatedly for about `seconds`; KV GB/s on the same algorithmic bytes."""
+    import numpy as np
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    case = workloads.qwen3_4b_decode(poison=False)
+    as_bits = lambda t: t.contiguous().view(__import__("torch").int16).numpy().view(np.uint16)  # noqa
+    kc, vc, q = as_bits(case.k_cache), as_bits(case.v_cache), as_bits(case.q)
+    bt, ctx = case.block_tables.numpy(), case.context_lens.numpy()
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode(q, kc, vc, bt, ctx, case.scale, case.num_q_heads, case.num_kv_heads)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per = el / runs
+    return {"value": round(case.kv_bytes() / per / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{runs} oracle decode(s) of one qwen3_4b_decode_b8 layer "
+                      f"({case.kv_bytes()} KV bytes each), {el:.1f} s total, "
+                      f"{per:.3f} s per layer; BLAS threads {threads}, gather loop single-threaded"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,194 @@
+/*
+ * pa.h -- grouped-query attention over a paged KV cache, for AMD Instinct
+ * MI355X (gfx950).  C ABI: plain device pointers, sizes and an opaque HIP
+ * stream handle; no framework types.
+ *
+ * What the operations compute comes from the serving pages this library
+ * follows ("Qwen3-4B / 8B / 32B", section Architecture Notes; "Qwen3.5-4B /
+ * 9B / 27B" and "Qwen3.5 Dense" for the hybrid models' full-attention
+ * layers):
+ *   - full attention with grouped-query attention: Hq query heads share Hkv
+ *     KV heads (32/8 for Qwen3-4B, group 8 for Qwen3-32B); query head h reads
+ *     KV head h / (Hq/Hkv);
+ *   - a paged KV cache with full-lifetime admission (a sequence's block-table
+ *     row may already list blocks past its current length; those entries are
+ *     never read);
+ *   - prefix caching on by default: a prefill attends to cached prefix blocks
+ *     and computes only the new tokens ("Qwen3-4B / 8B / 32B", section Warm
+ *     Prefix-Cache TTFT).
+ * Attention is scaled dot-product softmax attention,
+ *   out = sum_j exp(z_j) v_j / sum_j exp(z_j),   z_j = scale * <q, k_j>,
+ * computed with fp32 accumulation and bf16 inputs/outputs.
+ *
+ * ---------------------------------------------------------------------------
+ * Memory layout (all tensors row-major and contiguous; bf16 = 16-bit storage)
+ * ---------------------------------------------------------------------------
+ *   block_size (BS) is 16 tokens.
+ *   K pool   [num_blocks, Hkv, 16, D]  bf16: K row of the token at in-block
+ *            offset o of block b for KV head g starts at ((b*Hkv+g)*16+o)*D.
+ *   V pool   [num_blocks, Hkv, D, 16]  bf16: "transposed" -- element d of
+ *            that token's V row is at ((b*Hkv+g)*D+d)*16+o.  Each (block,
+ *            head) of either pool is one contiguous 16*D*2-byte tile.
+ *   slot     b*16 + o names a token's place in the pools.
+ *   block_tables [num_seqs, max_blocks_per_seq] int32: logical block i of
+ *            sequence s (positions 16i..16i+15) is physical block
+ *            block_tables[s*max_blocks_per_seq + i].
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions shared by every call
+ * ---------------------------------------------------------------------------
+ *   Ownership: the caller allocates and owns every buffer, including the
+ *     split-K workspace.  The library never allocates, frees or
+ *     synchronises; each call only enqueues kernels on `stream` (a
+ *     hipStream_t passed as void*; NULL = the default stream), so calls are
+ *     asynchronous, stateless, thread-safe and may be captured in a HIP graph.
+ *   Errors: arguments are checked on the host before anything is enqueued;
+ *     on failure the call returns a negative pa_status and writes nothing.
+ *     A failed kernel launch returns PA_ERR_LAUNCH.
+ *   Device-side data (table entries, lengths, slots) is validated by the
+ *     kernels without ever addressing memory outside the buffers described by
+ *     the size arguments: a block-table entry outside [0, num_blocks) that a
+ *     live position needs, a length that exceeds max_blocks_per_seq*16, or a
+ *     decode context longer than partition_size*num_partitions makes the
+ *     affected sequence's outputs NaN (and its split-K LSEs NaN).
+ *   Supported shapes: head_dim in {64, 128, 256}; num_q_heads a multiple of
+ *     num_kv_heads with a group Hq/Hkv of at most 16; block_size == 16.
+ *   Sizes of 0 (no tokens, no sequences) are valid no-ops.
+ */
+#ifndef PAGED_KV_GQA_PA_H
+#define PAGED_KV_GQA_PA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1,  /* null pointer, negative size, inconsistent sizes */
+  PA_ERR_UNSUPPORTED = -2,  /* head_dim / group / block_size outside the supported set */
+  PA_ERR_LAUNCH = -3        /* the HIP runtime rejected a kernel launch */
+} pa_status;
+
+/*
+ * pa_write_kv -- slot-mapped KV append (the write side of the paged KV cache,
+ * "Qwen3-4B / 8B / 32B", Architecture Notes).
+ *
+ * For every token t in [0, num_tokens) with slot = slot_mapping[t] >= 0:
+ *   K pool row of (slot/16, head g, offset slot%16) := k_new[t, g, :]
+ *   V pool column of (slot/16, head g, offset slot%16) := v_new[t, g, :]
+ * for all KV heads g.  Pure bit copies (bit-exact).  Slots < 0 are skipped;
+ * slots >= num_blocks*16 are invalid and skipped as well (never written).
+ * Two tokens naming the same slot race (last writer unspecified).
+ *
+ *   k_new, v_new   device, bf16 [num_tokens, Hkv, D]
+ *   slot_mapping   device, int64 [num_tokens]
+ *   k_cache        device, bf16 K pool (layout above), updated in place
+ *   v_cache        device, bf16 V pool (layout above), updated in place
+ */
+int pa_write_kv(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                void* k_cache, void* v_cache,
+                int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                int32_t block_size, int64_t num_blocks, void* stream);
+
+/*
+ * pa_decode -- one query token per sequence attends over its paged context
+ * (decode of the full-attention layers; "Qwen3-4B / 8B / 32B", Architecture
+ * Notes).  Sequence s's query sits at position context_lens[s]-1 and sees
+ * keys 0..context_lens[s]-1 (its own K/V must already be in the pool, e.g.
+ * written by pa_write_kv on the same stream).
+ *
+ * Split-K: the context is cut into partitions of partition_size tokens
+ * (partition p covers positions [p*ps, (p+1)*ps)).
+ *   num_partitions == 1: writes out[s, h, :] (bf16) directly; part_out and
+ *     part_lse are not used and may be NULL.
+ *   num_partitions  > 1: writes, for every (s, h, p),
+ *       part_out[s, h, p, :] = sum_{j in p} e^{z_j} v_j / sum_{j in p} e^{z_j}
+ *       part_lse[s, h, p]    = ln sum_{j in p} e^{z_j}
+ *     (fp32; an empty partition gives 0 and -inf); `out` is not touched and
+ *     may be NULL.  pa_decode_reduce then produces `out`.
+ *   num_partitions*partition_size must cover every context length.
+ *
+ *   out            device, bf16 [num_seqs, Hq, D]
+ *   part_out       device, fp32 [num_seqs, Hq, num_partitions, D]
+ *   part_lse       device, fp32 [num_seqs, Hq, num_partitions]
+ *   q              device, bf16 [num_seqs, Hq, D]
+ *   k_cache, v_cache   device, pools (layout above)
+ *   block_tables   device, int32 [num_seqs, max_blocks_per_seq]
+ *   context_lens   device, int32 [num_seqs] (0 gives a zero output)
+ *   partition_size multiple of 16, > 0
+ *   scale          softmax scale applied to <q, k> in fp32 (e.g. 1/sqrt(D))
+ */
+int pa_decode(void* out, float* part_out, float* part_lse,
+              const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens,
+              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+              int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
+              int32_t partition_size, int32_t num_partitions,
+              float scale, void* stream);
+
+/*
+ * pa_decode_reduce -- log-sum-exp combination of pa_decode's split-K pieces:
+ *   M = max_p lse_p,  w_p = e^{lse_p - M},
+ *   out[s, h, :] = bf16( sum_p w_p part_out[s, h, p, :] / sum_p w_p ),
+ * zero when every partition is empty; NaN when any read LSE is NaN.
+ *
+ *   context_lens   device int32 [num_seqs] or NULL.  When given, only the
+ *                  partitions p < ceil(ctx/partition_size) are read; when
+ *                  NULL all num_partitions are read (empty ones must hold
+ *                  lse = -inf, as pa_decode writes them).
+ *   other arguments as for pa_decode.
+ */
+int pa_decode_reduce(void* out, const float* part_out, const float* part_lse,
+                     const int32_t* context_lens,
+                     int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                     int32_t partition_size, int32_t num_partitions, void* stream);
+
+/*
+ * pa_prefill -- varlen causal prefill over the paged cache with cached
+ * prefixes ("Qwen3-4B / 8B / 32B", sections Warm Prefix-Cache TTFT and
+ * Architecture Notes: prefix cache on by default).
+ *
+ * Sequence s has n_s = cu_seqlens[s+1]-cu_seqlens[s] new tokens following
+ * p_s = prefix_lens[s] cached ones.  New token i (packed row cu_seqlens[s]+i)
+ * sits at position p_s+i and attends to keys 0..p_s+i, all read through the
+ * block table (the new tokens' K/V must already be in the pool).
+ *
+ *   out            device, bf16 [total_q, Hq, D]
+ *   q              device, bf16 [total_q, Hq, D] (packed varlen)
+ *   k_cache, v_cache   device, pools (layout above)
+ *   block_tables   device, int32 [num_seqs, max_blocks_per_seq]
+ *   cu_seqlens     device, int32 [num_seqs+1], non-decreasing, from 0 to
+ *                  total_q (rows of a sequence whose range leaves
+ *                  [0, total_q] are not written)
+ *   prefix_lens    device, int32 [num_seqs], or NULL for no cached prefixes
+ *   max_q_len      host upper bound of n_s (sizes the launch grid; rows of
+ *                  a sequence beyond it are not written)
+ */
+int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_tables, const int32_t* cu_seqlens,
+               const int32_t* prefix_lens,
+               int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+               int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
+               float scale, void* stream);
+
+/*
+ * pa_decode_split_plan -- host-only helper: a partition size (multiple of
+ * 16) and count for pa_decode that give the GPU enough independent work
+ * items while covering max_context_len.  Writes *partition_size and
+ * *num_partitions; returns PA_OK or PA_ERR_INVALID_ARG.
+ */
+int pa_decode_split_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                         int32_t num_compute_units,
+                         int32_t* partition_size, int32_t* num_partitions);
+
+/* Host-only: a static string naming a pa_status value. */
+const char* pa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_KV_GQA_PA_H */

@@ -1,0 +1,243 @@
+"""Grouped-query attention over a paged KV cache on AMD Instinct MI355X.
+
+Thin ctypes binding of the C ABI in include/pa.h (libpa.so, built by
+paged_kv_gqa_write_amd/build.py).  PyTorch supplies device memory and the
+current HIP stream; every step of the computation runs in the library's HIP
+kernels.  There is no fallback: if the library is missing, every call
+raises.
+
+Pool layout (see include/pa.h):
+  k_cache [num_blocks, Hkv, 16, D] bf16,  v_cache [num_blocks, Hkv, D, 16] bf16.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "PAError", "load_library", "library_path", "write_kv", "decode", "decode_partials",
+    "decode_reduce", "prefill", "decode_split_plan", "status_string", "EXPORTED_SYMBOLS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libpa.so")
+_lib = None
+
+BLOCK_SIZE = 16
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_LAUNCH = 0, -1, -2, -3
+
+_vp, _i32, _i64, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+_pi32 = ctypes.POINTER(ctypes.c_int32)
+
+# name -> (restype, argtypes); mirrors include/pa.h
+_SIGNATURES = {
+    "pa_write_kv": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _vp]),
+    "pa_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                 _i32, _i64, _i32, _i32, _i32, _f32, _vp]),
+    "pa_decode_reduce": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pa_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                  _i32, _i32, _i32, _i64, _i32, _f32, _vp]),
+    "pa_decode_split_plan": (ctypes.c_int, [_i32, _i32, _i32, _i32, _pi32, _pi32]),
+    "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+}
+EXPORTED_SYMBOLS = tuple(_SIGNATURES)
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library(path: str | None = None):
+    """Load libpa.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or _LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(
+            f"HIP library not found at {p}; build it with "
+            "`python -m paged_kv_gqa_write_amd.build` (there is no fallback path)")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().pa_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != PA_OK:
+        raise PAError(status, where)
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int | None = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _pools(k_cache, v_cache):
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    nb, hkv, bs, d = k_cache.shape
+    if bs != BLOCK_SIZE or tuple(v_cache.shape) != (nb, hkv, d, BLOCK_SIZE):
+        raise ValueError("pools must be K [NB, Hkv, 16, D] and V [NB, Hkv, D, 16]; got "
+                         f"{tuple(k_cache.shape)} and {tuple(v_cache.shape)}")
+    return nb, hkv, d
+
+
+def write_kv(k_new, v_new, slot_mapping, k_cache, v_cache):
+    """Write each token's K/V into its slot (slot < 0: skipped)."""
+    nb, hkv, d = _pools(k_cache, v_cache)
+    _need(k_new, "k_new", torch.bfloat16, 3)
+    _need(v_new, "v_new", torch.bfloat16, 3)
+    _need(slot_mapping, "slot_mapping", torch.int64, 1)
+    T = k_new.shape[0]
+    if tuple(k_new.shape) != (T, hkv, d) or tuple(v_new.shape) != (T, hkv, d) \
+            or slot_mapping.shape[0] != T:
+        raise ValueError("k_new/v_new must be [T, Hkv, D] and slot_mapping [T]")
+    st = load_library().pa_write_kv(k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(),
+                                    k_cache.data_ptr(), v_cache.data_ptr(), T, hkv, d,
+                                    BLOCK_SIZE, nb, _stream(k_cache.device))
+    _check(st, "pa_write_kv")
+
+
+def decode_split_plan(num_seqs: int, num_kv_heads: int, max_context_len: int,
+                      num_compute_units: int | None = None):
+    """(partition_size, num_partitions) from the library's host heuristic."""
+    if num_compute_units is None:
+        num_compute_units = torch.cuda.get_device_properties(0).multi_processor_count
+    ps, npart = ctypes.c_int32(0), ctypes.c_int32(0)
+    st = load_library().pa_decode_split_plan(int(num_seqs), int(num_kv_heads),
+                                             int(max_context_len), int(num_compute_units),
+                                             ctypes.byref(ps), ctypes.byref(npart))
+    _check(st, "pa_decode_split_plan")
+    return ps.value, npart.value
+
+
+def _decode_call(out, part_out, part_lse, q, k_cache, v_cache, block_tables, context_lens,
+                 scale, partition_size, num_partitions):
+    nb, hkv, d = _pools(k_cache, v_cache)
+    _need(q, "q", torch.bfloat16, 3)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    B, hq, dq = q.shape
+    if dq != d or block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("q [B, Hq, D], block_tables [B, max_blocks], context_lens [B] mismatch")
+    ptr = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
+    st = load_library().pa_decode(ptr(out), ptr(part_out), ptr(part_lse), q.data_ptr(),
+                                  k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+                                  context_lens.data_ptr(), B, hq, hkv, d, BLOCK_SIZE, nb,
+                                  block_tables.shape[1], int(partition_size),
+                                  int(num_partitions), float(scale), _stream(q.device))
+    _check(st, "pa_decode")
+
+
+def decode_partials(q, k_cache, v_cache, block_tables, context_lens, scale, partition_size,
+                    num_partitions, part_out=None, part_lse=None):
+    """Split-K pieces only (num_partitions > 1): (part_out [B,Hq,P,D], part_lse [B,Hq,P])."""
+    B, hq, d = q.shape
+    if part_out is None:
+        part_out = torch.empty(B, hq, num_partitions, d, dtype=torch.float32, device=q.device)
+    if part_lse is None:
+        part_lse = torch.empty(B, hq, num_partitions, dtype=torch.float32, device=q.device)
+    _decode_call(None, part_out, part_lse, q, k_cache, v_cache, block_tables, context_lens,
+                 scale, partition_size, num_partitions)
+    return part_out, part_lse
+
+
+def decode_reduce(part_out, part_lse, context_lens, partition_size, out=None):
+    """Log-sum-exp combine of split-K pieces into bf16 [B, Hq, D]."""
+    _need(part_out, "part_out", torch.float32, 4)
+    _need(part_lse, "part_lse", torch.float32, 3)
+    B, hq, P, d = part_out.shape
+    if context_lens is not None:
+        _need(context_lens, "context_lens", torch.int32, 1)
+    if out is None:
+        out = torch.empty(B, hq, d, dtype=torch.bfloat16, device=part_out.device)
+    st = load_library().pa_decode_reduce(out.data_ptr(), part_out.data_ptr(), part_lse.data_ptr(),
+                                         0 if context_lens is None else context_lens.data_ptr(),
+                                         B, hq, d, int(partition_size), P,
+                                         _stream(part_out.device))
+    _check(st, "pa_decode_reduce")
+    return out
+
+
+def decode(q, k_cache, v_cache, block_tables, context_lens, scale, *, max_context_len=None,
+           partition_size=None, num_partitions=None, out=None, part_out=None, part_lse=None):
+    """Decode attention, one query token per sequence -> bf16 [B, Hq, D].
+
+    The split-K plan comes from the library heuristic unless given; with more
+    than one partition the pieces are combined by pa_decode_reduce."""
+    B, hq, d = q.shape
+    if out is None:
+        out = torch.empty(B, hq, d, dtype=torch.bfloat16, device=q.device)
+    if partition_size is None:
+        if max_context_len is None:
+            max_context_len = int(context_lens.max().item()) if B > 0 else 0
+        partition_size, num_partitions = decode_split_plan(B, k_cache.shape[1], max_context_len)
+    elif num_partitions is None:
+        if max_context_len is None:
+            max_context_len = int(context_lens.max().item()) if B > 0 else 0
+        num_partitions = max(1, -(-max_context_len // partition_size))
+    if num_partitions == 1:
+        _decode_call(out, None, None, q, k_cache, v_cache, block_tables, context_lens, scale,
+                     partition_size, 1)
+        return out
+    part_out, part_lse = decode_partials(q, k_cache, v_cache, block_tables, context_lens, scale,
+                                         partition_size, num_partitions, part_out, part_lse)
+    return decode_reduce(part_out, part_lse, context_lens, partition_size, out=out)
+
+
+def prefill(q, k_cache, v_cache, block_tables, cu_seqlens, prefix_lens, scale, max_q_len,
+            out=None):
+    """Varlen causal prefill with cached prefixes -> bf16 [total_q, Hq, D].
+
+    max_q_len is a host-side upper bound of the per-sequence new-token count."""
+    nb, hkv, d = _pools(k_cache, v_cache)
+    _need(q, "q", torch.bfloat16, 3)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    S = cu_seqlens.shape[0] - 1
+    if prefix_lens is not None:
+        _need(prefix_lens, "prefix_lens", torch.int32, 1)
+        if prefix_lens.shape[0] != S:
+            raise ValueError("prefix_lens must be [num_seqs]")
+    total_q, hq, dq = q.shape
+    if dq != d or block_tables.shape[0] != S:
+        raise ValueError("q [total_q, Hq, D] / block_tables [S, max_blocks] mismatch")
+    if out is None:
+        out = torch.empty_like(q)
+    st = load_library().pa_prefill(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(),
+                                   v_cache.data_ptr(), block_tables.data_ptr(),
+                                   cu_seqlens.data_ptr(),
+                                   0 if prefix_lens is None else prefix_lens.data_ptr(),
+                                   S, total_q, int(max_q_len), hq, hkv, d, BLOCK_SIZE, nb,
+                                   block_tables.shape[1], float(scale), _stream(q.device))
+    _check(st, "pa_prefill")
+    return out

@@ -1,0 +1,402 @@
+// Paged GQA decode: split-K flash-decoding over block-tabled KV, plus the
+// log-sum-exp reduce of the split-K pieces.
+//
+// Work decomposition: one workgroup per (partition p, KV head g, sequence s),
+// NW waves per workgroup.  The partition's KV blocks are taken two at a time
+// ("pairs", 32 keys); wave w handles pairs w, w+NW, ...  All G query heads of
+// the KV head are processed together, so each K/V byte is read once.
+//
+// Both contractions run on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16),
+// with the query heads as the 16-wide N dimension (zero-padded when G < 16):
+//   S^T[key][head]  = K[key][:]   . Q^T[:][head]   (A = K rows, B = Q)
+//   O^T[d][head]   += V^T[d][key] . P^T[key][head] (A = V^T rows, B = P)
+// The score accumulator layout (lane l holds rows 4*(l/16)+r of column l%16)
+// is chosen to be exactly the B-operand layout of the P.V product, so P never
+// leaves registers: the 16 key rows of the two score tiles are a permutation
+// of the pair's 32 keys such that lane group c ends up holding 8 consecutive
+// keys of one block, which is also what one 16-byte load of a V^T row gives.
+// K and V bytes go from HBM straight into MFMA operand registers with 16-byte
+// loads; the next pair's loads are issued before the current pair is used.
+//
+// Softmax is online (running max m, running sum l per head, base-2
+// exponentials with scale*log2(e) folded in); m is made uniform across the
+// four lane groups of a head with two cross-lane max steps per pair, l is
+// kept per lane and summed once at the end.  P enters the matrix core as a
+// bf16 hi/lo pair (two products), which keeps its rounding error far below
+// the bf16 output rounding; decode is memory-bound, so the extra products
+// cost no time.  Waves are merged through LDS.
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+
+namespace {
+
+constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kLog2e = 1.44269504088896341f;
+
+template <int D>
+struct PairRegs {
+  u32x4 k[2][D / 32];  // two score tiles x D/32 k-steps (A operand of S^T)
+  u32x4 v[D / 16];     // D/16 d-tiles (A operand of O^T)
+};
+
+// Issue the loads of pair j (blocks x, x+1 of the sequence).  Lanes whose
+// block does not exist or is unusable get zeros; their keys are masked.
+template <int D>
+__device__ __forceinline__ void load_pair(PairRegs<D>& r, const uint16_t* __restrict__ k_cache,
+                                          const uint16_t* __restrict__ v_cache, int64_t physx,
+                                          bool okx, int64_t physy, bool oky, int g, int hkv,
+                                          int col, int c) {
+  // K: score-tile row `col` -> key: group gr = col/4 picks the block (gr >= 2
+  // -> second block) and the 4-key run 8*(gr&1) (+4 for the second tile).
+  {
+    const int gr = col >> 2;
+    const bool sel_y = gr >= 2;
+    const int key = 8 * (gr & 1) + (col & 3);
+    const bool ok = sel_y ? oky : okx;
+    const int64_t phys = sel_y ? physy : physx;
+    const uint16_t* base = k_cache + ((phys * hkv + g) * kBlock + key) * D + 8 * c;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+        r.k[t][i] = ok ? load16_stream(base + t * 4 * D + 32 * i) : u32x4{0, 0, 0, 0};
+  }
+  // V^T: lane group c reads keys 8*(c&1)..+8 of block (c >= 2 ? y : x), for
+  // d row 16*dt + col.
+  {
+    const bool sel_y = c >= 2;
+    const bool ok = sel_y ? oky : okx;
+    const int64_t phys = sel_y ? physy : physx;
+    const uint16_t* base = v_cache + ((phys * hkv + g) * D + col) * kBlock + 8 * (c & 1);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+      r.v[dt] = ok ? load16_stream(base + dt * 16 * kBlock) : u32x4{0, 0, 0, 0};
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void compute_pair(PairRegs<D>& r, const u32x4 (&qf)[D / 32],
+                                             f32x4 (&acc)[D / 16], float& m_run, float& l_run,
+                                             int base_pos, int limit, float scale_log2) {
+  // Scores: tile 0 holds keys 8*(c&1)+0..3, tile 1 keys 8*(c&1)+4..7 of the
+  // lane group's block.
+  f32x4 s0 = {0, 0, 0, 0}, s1 = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    s0 = mfma16x16x32(r.k[0][i], qf[i], s0);
+    s1 = mfma16x16x32(r.k[1][i], qf[i], s1);
+  }
+  float sc[8];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    sc[t] = (base_pos + t < limit) ? s0[t] * scale_log2 : -INFINITY;
+    sc[t + 4] = (base_pos + 4 + t < limit) ? s1[t] * scale_log2 : -INFINITY;
+  }
+  float mx = sc[0];
+#pragma unroll
+  for (int t = 1; t < 8; ++t) mx = fmaxf(mx, sc[t]);
+  mx = wave_xor_max(mx, 16);
+  mx = wave_xor_max(mx, 32);
+  const float m_new = fmaxf(m_run, mx);
+  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+  const float alpha = fast_exp2(m_run - m_use);
+  // P as a bf16 hi + lo pair: the two products together carry ~16 mantissa
+  // bits of P, so rounding P costs nothing even when a few keys dominate.
+  u32x4 pb_hi, pb_lo;
+  float psum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float a = fast_exp2(sc[2 * e] - m_use);
+    const float b = fast_exp2(sc[2 * e + 1] - m_use);
+    const uint32_t hi = pack_bf16x2(a, b);
+    pb_hi[e] = hi;
+    pb_lo[e] = pack_bf16x2(a - bf16_bits_to_f32(hi & 0xFFFFu), b - bf16_bits_to_f32(hi >> 16));
+    psum += a + b;
+  }
+  l_run = l_run * alpha + psum;
+  m_run = m_new;
+  // Keys past the valid range may hold anything (NaN included); their P is 0
+  // but 0*NaN is NaN, so zero their V values before the product.
+  if (base_pos + 8 > limit) {
+    u32x4 keep;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      keep[e] = ((base_pos + 2 * e < limit) ? 0x0000FFFFu : 0u) |
+                ((base_pos + 2 * e + 1 < limit) ? 0xFFFF0000u : 0u);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) r.v[dt] &= keep;
+  }
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    acc[dt] *= alpha;
+    acc[dt] = mfma16x16x32(r.v[dt], pb_hi, acc[dt]);
+    acc[dt] = mfma16x16x32(r.v[dt], pb_lo, acc[dt]);
+  }
+}
+
+// Physical blocks of pair j; flags a table entry outside the pool.
+__device__ __forceinline__ void pair_blocks(const int32_t* __restrict__ bt, int pb0, int pb1,
+                                            int j, int64_t num_blocks, int64_t& px, bool& okx,
+                                            int64_t& py, bool& oky, bool& bad) {
+  const int bx = pb0 + 2 * j;
+  px = bt[bx];
+  okx = px >= 0 && px < num_blocks;
+  const bool hy = bx + 1 < pb1;
+  py = hy ? (int64_t)bt[bx + 1] : 0;
+  oky = hy && py >= 0 && py < num_blocks;
+  bad |= !okx || (hy && !oky);
+}
+
+template <int D, int NW, bool PREFETCH>
+__global__ __launch_bounds__(NW * 64) void decode_kernel(
+    uint16_t* __restrict__ out, float* __restrict__ part_out, float* __restrict__ part_lse,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
+    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ context_lens, int num_q_heads, int num_kv_heads, int group,
+    int64_t num_blocks, int max_blocks, int blocks_per_part, int num_partitions,
+    float scale_log2) {
+  constexpr int KS = D / 32;
+  constexpr int DT = D / 16;
+  const int wg = blockIdx.x;
+  const int p = wg % num_partitions;
+  const int g = (wg / num_partitions) % num_kv_heads;
+  const int s = wg / (num_partitions * num_kv_heads);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int c = lane >> 4;
+
+  const int ctx = context_lens[s];
+  const int nblk = ctx > 0 ? (ctx + kBlock - 1) / kBlock : 0;
+  bool bad = ctx < 0 || nblk > max_blocks ||
+             (int64_t)ctx > (int64_t)num_partitions * blocks_per_part * kBlock;
+  const int pb0 = p * blocks_per_part;
+  const int pb1 = bad ? pb0 : min(pb0 + blocks_per_part, nblk);
+  const int limit = min(ctx, pb1 * kBlock);
+  const int npairs = pb1 > pb0 ? (pb1 - pb0 + 1) / 2 : 0;
+
+  u32x4 qf[KS];
+  {
+    const bool has = col < group;
+    const uint16_t* qb = q + ((int64_t)s * num_q_heads + (int64_t)g * group + col) * D + 8 * c;
+#pragma unroll
+    for (int i = 0; i < KS; ++i) qf[i] = has ? load16(qb + 32 * i) : u32x4{0, 0, 0, 0};
+  }
+
+  f32x4 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0, 0, 0, 0};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int32_t* bt = block_tables + (int64_t)s * max_blocks;
+  // Lane group c's keys start at block (c >= 2 ? y : x), offset 8*(c&1).
+  const int lane_key0 = ((c >= 2) ? kBlock : 0) + 8 * (c & 1);
+  int64_t px, py;
+  bool okx, oky;
+
+  if (PREFETCH) {
+    // Two register sets used alternately: the loads of the next pair are in
+    // flight while the current one is consumed.
+    PairRegs<D> ra, rb;
+    int j = wave;
+    if (j < npairs) {
+      pair_blocks(bt, pb0, pb1, j, num_blocks, px, okx, py, oky, bad);
+      load_pair<D>(ra, k_cache, v_cache, px, okx, py, oky, g, num_kv_heads, col, c);
+    }
+    for (; j < npairs; j += 2 * NW) {
+      if (j + NW < npairs) {
+        pair_blocks(bt, pb0, pb1, j + NW, num_blocks, px, okx, py, oky, bad);
+        load_pair<D>(rb, k_cache, v_cache, px, okx, py, oky, g, num_kv_heads, col, c);
+      }
+      compute_pair<D>(ra, qf, acc, m_run, l_run, (pb0 + 2 * j) * kBlock + lane_key0, limit,
+                      scale_log2);
+      if (j + NW >= npairs) break;
+      if (j + 2 * NW < npairs) {
+        pair_blocks(bt, pb0, pb1, j + 2 * NW, num_blocks, px, okx, py, oky, bad);
+        load_pair<D>(ra, k_cache, v_cache, px, okx, py, oky, g, num_kv_heads, col, c);
+      }
+      compute_pair<D>(rb, qf, acc, m_run, l_run, (pb0 + 2 * (j + NW)) * kBlock + lane_key0,
+                      limit, scale_log2);
+    }
+  } else {
+    for (int j = wave; j < npairs; j += NW) {
+      PairRegs<D> ra;
+      pair_blocks(bt, pb0, pb1, j, num_blocks, px, okx, py, oky, bad);
+      load_pair<D>(ra, k_cache, v_cache, px, okx, py, oky, g, num_kv_heads, col, c);
+      compute_pair<D>(ra, qf, acc, m_run, l_run, (pb0 + 2 * j) * kBlock + lane_key0, limit,
+                      scale_log2);
+    }
+  }
+
+  // Per-wave totals: l over the four lane groups of each head.
+  l_run = wave_xor_sum(l_run, 16);
+  l_run = wave_xor_sum(l_run, 32);
+
+  // Merge the NW waves: common max M per head, then waves 1..NW-1 hand their
+  // rescaled accumulators to wave 0 through LDS (fixed order: deterministic).
+  __shared__ float sm_m[NW][16];
+  __shared__ float sm_l[NW][16];
+  __shared__ f32x4 sm_o[NW > 1 ? NW - 1 : 1][DT][64];
+  if (lane < 16) {
+    sm_m[wave][col] = m_run;
+    sm_l[wave][col] = l_run;
+  }
+  const bool any_bad = __syncthreads_or(bad);
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][col]);
+  float L = 0.f, f = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) L += sm_l[w][col] * fast_exp2(sm_m[w][col] - M);
+    f = fast_exp2(m_run - M);
+  }
+  if (NW > 1) {
+    if (wave > 0) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) sm_o[wave - 1][dt][lane] = acc[dt] * f;
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      f32x4 a = acc[dt] * f;
+#pragma unroll
+      for (int w = 0; w < NW - 1; ++w) a += sm_o[w][dt][lane];
+      acc[dt] = a;
+    }
+  } else {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] *= f;
+  }
+
+  // Wave 0 writes: lane (col, c) holds head col, d = 16*dt + 4*c + r.
+  if (col >= group) return;
+  const int64_t head = (int64_t)s * num_q_heads + (int64_t)g * group + col;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const float nanv = __builtin_nanf("");
+  if (num_partitions == 1) {
+    uint16_t* dst = out + head * D + 4 * c;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      f32x4 o = acc[dt] * inv;
+      if (any_bad) o = f32x4{nanv, nanv, nanv, nanv};
+      u32x2 w;
+      w[0] = pack_bf16x2(o[0], o[1]);
+      w[1] = pack_bf16x2(o[2], o[3]);
+      *reinterpret_cast<u32x2*>(dst + 16 * dt) = w;
+    }
+  } else {
+    float* dst = part_out + (head * num_partitions + p) * D + 4 * c;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      f32x4 o = acc[dt] * inv;
+      if (any_bad) o = f32x4{nanv, nanv, nanv, nanv};
+      *reinterpret_cast<f32x4*>(dst + 16 * dt) = o;
+    }
+    if (c == 0) {
+      float lse = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
+      if (any_bad) lse = nanv;
+      part_lse[head * num_partitions + p] = lse;
+    }
+  }
+}
+
+// One wave per (sequence, query head).
+template <int D>
+__global__ __launch_bounds__(64) void decode_reduce_kernel(
+    uint16_t* __restrict__ out, const float* __restrict__ part_out,
+    const float* __restrict__ part_lse, const int32_t* __restrict__ context_lens,
+    int num_q_heads, int partition_size, int num_partitions) {
+  constexpr int EPT = D / 64;
+  const int64_t row = blockIdx.x;  // s * Hq + h
+  const int s = (int)(row / num_q_heads);
+  const int lane = threadIdx.x;
+  int np = num_partitions;
+  if (context_lens != nullptr) {
+    const int ctx = context_lens[s];
+    np = ctx <= 0 ? 0 : min(num_partitions, (ctx + partition_size - 1) / partition_size);
+  }
+  const float* lse = part_lse + row * num_partitions;
+  float M = -INFINITY;
+  bool nan_seen = false;
+  for (int p = lane; p < np; p += 64) {
+    const float v = lse[p];
+    nan_seen |= v != v;
+    M = fmaxf(M, v);
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) M = wave_xor_max(M, m);
+  nan_seen = __any(nan_seen);
+
+  float o[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) o[e] = 0.f;
+  float L = 0.f;
+  if (M != -INFINITY) {
+    const float* po = part_out + row * num_partitions * D + lane * EPT;
+    for (int p = 0; p < np; ++p) {
+      const float w = fast_exp2((lse[p] - M) * kLog2e);
+      L += w;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) o[e] += w * po[(int64_t)p * D + e];
+    }
+  }
+  uint16_t* dst = out + row * D + lane * EPT;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    float val = L > 0.f ? o[e] / L : 0.f;
+    if (nan_seen) val = __builtin_nanf("");
+    dst[e] = f32_to_bf16_bits(val);
+  }
+}
+
+}  // namespace
+
+int launch_decode(void* out, float* part_out, float* part_lse, const void* q,
+                  const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                  const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
+                  int head_dim, int64_t num_blocks, int max_blocks_per_seq, int partition_size,
+                  int num_partitions, float scale, hipStream_t stream) {
+  const int group = num_q_heads / num_kv_heads;
+  const int64_t nwg = (int64_t)num_partitions * num_kv_heads * num_seqs;
+  const float scale_log2 = scale * kLog2e;
+  const int bpp = partition_size / kBlock;
+  constexpr int NW = 4;
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(NW * 64), 0, stream, (uint16_t*)out,
+                       part_out, part_lse, (const uint16_t*)q, (const uint16_t*)k_cache,
+                       (const uint16_t*)v_cache, block_tables, context_lens, num_q_heads,
+                       num_kv_heads, group, num_blocks, max_blocks_per_seq, bpp,
+                       num_partitions, scale_log2);
+  };
+  switch (head_dim) {
+    case 64: go(decode_kernel<64, NW, true>); break;
+    case 128: go(decode_kernel<128, NW, true>); break;
+    case 256: go(decode_kernel<256, NW, false>); break;
+    default: return -2;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+int launch_decode_reduce(void* out, const float* part_out, const float* part_lse,
+                         const int32_t* context_lens, int num_seqs, int num_q_heads,
+                         int head_dim, int partition_size, int num_partitions,
+                         hipStream_t stream) {
+  const int64_t rows = (int64_t)num_seqs * num_q_heads;
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)rows), dim3(64), 0, stream, (uint16_t*)out, part_out,
+                       part_lse, context_lens, num_q_heads, partition_size, num_partitions);
+  };
+  switch (head_dim) {
+    case 64: go(decode_reduce_kernel<64>); break;
+    case 128: go(decode_reduce_kernel<128>); break;
+    case 256: go(decode_reduce_kernel<256>); break;
+    default: return -2;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+}  // namespace pa

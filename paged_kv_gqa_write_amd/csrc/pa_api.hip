@@ -1,0 +1,137 @@
+// C ABI of the paged GQA attention library: host-side argument validation,
+// then a launch on the caller's stream.  Nothing here allocates, frees or
+// synchronises.  Every check happens before any HIP call, so an invalid call
+// returns without touching the device.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/pa.h"
+#include "pa_launch.h"
+
+namespace {
+
+constexpr int kBlockSize = 16;
+constexpr int kMaxGroup = 16;
+constexpr int64_t kMaxGrid = 0x7FFFFFFF;
+
+bool supported_head_dim(int32_t d) { return d == 64 || d == 128 || d == 256; }
+
+int check_heads(int32_t hq, int32_t hkv, int32_t d, int32_t bs) {
+  if (hq <= 0 || hkv <= 0) return PA_ERR_INVALID_ARG;
+  if (hq % hkv != 0) return PA_ERR_INVALID_ARG;
+  if (hq / hkv > kMaxGroup) return PA_ERR_UNSUPPORTED;
+  if (!supported_head_dim(d)) return PA_ERR_UNSUPPORTED;
+  if (bs != kBlockSize) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int pa_write_kv(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                void* k_cache, void* v_cache, int32_t num_tokens, int32_t num_kv_heads,
+                int32_t head_dim, int32_t block_size, int64_t num_blocks, void* stream) {
+  if (num_tokens < 0 || num_blocks < 0 || num_kv_heads <= 0) return PA_ERR_INVALID_ARG;
+  if (!supported_head_dim(head_dim) || block_size != kBlockSize) return PA_ERR_UNSUPPORTED;
+  if (num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PA_ERR_INVALID_ARG;
+  return pa::launch_write_kv(k_new, v_new, slot_mapping, k_cache, v_cache, num_tokens,
+                             num_kv_heads, head_dim, num_blocks, as_stream(stream));
+}
+
+int pa_decode(void* out, float* part_out, float* part_lse, const void* q, const void* k_cache,
+              const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+              int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
+              int32_t partition_size, int32_t num_partitions, float scale, void* stream) {
+  if (num_seqs < 0 || num_blocks < 0) return PA_ERR_INVALID_ARG;
+  int st = check_heads(num_q_heads, num_kv_heads, head_dim, block_size);
+  if (st != PA_OK) return st;
+  if (max_blocks_per_seq <= 0) return PA_ERR_INVALID_ARG;
+  if (partition_size <= 0 || partition_size % kBlockSize != 0) return PA_ERR_INVALID_ARG;
+  if (num_partitions < 1) return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if ((int64_t)num_partitions * num_kv_heads * num_seqs > kMaxGrid) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
+  if (num_partitions == 1 && !out) return PA_ERR_INVALID_ARG;
+  if (num_partitions > 1 && (!part_out || !part_lse)) return PA_ERR_INVALID_ARG;
+  return pa::launch_decode(out, part_out, part_lse, q, k_cache, v_cache, block_tables,
+                           context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                           num_blocks, max_blocks_per_seq, partition_size, num_partitions,
+                           scale, as_stream(stream));
+}
+
+int pa_decode_reduce(void* out, const float* part_out, const float* part_lse,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                     int32_t head_dim, int32_t partition_size, int32_t num_partitions,
+                     void* stream) {
+  if (num_seqs < 0 || num_q_heads <= 0) return PA_ERR_INVALID_ARG;
+  if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+  if (partition_size <= 0 || partition_size % kBlockSize != 0) return PA_ERR_INVALID_ARG;
+  if (num_partitions < 1) return PA_ERR_INVALID_ARG;
+  if ((int64_t)num_seqs * num_q_heads > kMaxGrid) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !part_out || !part_lse) return PA_ERR_INVALID_ARG;
+  return pa::launch_decode_reduce(out, part_out, part_lse, context_lens, num_seqs, num_q_heads,
+                                  head_dim, partition_size, num_partitions, as_stream(stream));
+}
+
+int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_tables, const int32_t* cu_seqlens,
+               const int32_t* prefix_lens, int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+               int64_t num_blocks, int32_t max_blocks_per_seq, float scale, void* stream) {
+  if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || num_blocks < 0) return PA_ERR_INVALID_ARG;
+  int st = check_heads(num_q_heads, num_kv_heads, head_dim, block_size);
+  if (st != PA_OK) return st;
+  if (max_blocks_per_seq <= 0) return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !cu_seqlens)
+    return PA_ERR_INVALID_ARG;
+  return pa::launch_prefill(out, q, k_cache, v_cache, block_tables, cu_seqlens, prefix_lens,
+                            num_seqs, total_q, max_q_len, num_q_heads, num_kv_heads, head_dim,
+                            num_blocks, max_blocks_per_seq, scale, as_stream(stream));
+}
+
+int pa_decode_split_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                         int32_t num_compute_units, int32_t* partition_size,
+                         int32_t* num_partitions) {
+  if (!partition_size || !num_partitions) return PA_ERR_INVALID_ARG;
+  if (num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0 || num_compute_units <= 0)
+    return PA_ERR_INVALID_ARG;
+  // Aim for at least two workgroups per compute unit.  A partition is a
+  // multiple of 128 tokens (one 32-key pair for each of the 4 waves of a
+  // workgroup), so every wave of a workgroup gets the same number of pairs.
+  constexpr int64_t kUnit = 128;
+  const int64_t items = (int64_t)num_seqs * num_kv_heads;
+  const int64_t ctx = max_context_len > 0 ? max_context_len : 1;
+  const int64_t want = 2LL * num_compute_units;
+  int64_t parts = items > 0 ? (want + items - 1) / items : 1;
+  if (parts < 1) parts = 1;
+  int64_t ps = (ctx + parts - 1) / parts;
+  ps = ((ps + kUnit - 1) / kUnit) * kUnit;
+  int64_t np = (ctx + ps - 1) / ps;
+  if (np == 1) ps = ((ctx + kBlockSize - 1) / kBlockSize) * kBlockSize;
+  if (ps > 0x7FFFFFF0LL) return PA_ERR_INVALID_ARG;
+  *partition_size = (int32_t)ps;
+  *num_partitions = (int32_t)np;
+  return PA_OK;
+}
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG: invalid argument";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: unsupported shape";
+    case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: kernel launch failed";
+    default: return "unknown pa_status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,33 @@
+// Internal launcher interface between the C ABI (pa_api.hip) and the kernel
+// translation units.  Arguments are already validated by the caller; each
+// launcher returns 0, -2 (no kernel instance for the shape) or -3 (launch
+// rejected by the runtime).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+int launch_write_kv(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                    void* k_cache, void* v_cache, int num_tokens, int num_kv_heads,
+                    int head_dim, int64_t num_blocks, hipStream_t stream);
+
+int launch_decode(void* out, float* part_out, float* part_lse, const void* q,
+                  const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                  const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
+                  int head_dim, int64_t num_blocks, int max_blocks_per_seq, int partition_size,
+                  int num_partitions, float scale, hipStream_t stream);
+
+int launch_decode_reduce(void* out, const float* part_out, const float* part_lse,
+                         const int32_t* context_lens, int num_seqs, int num_q_heads,
+                         int head_dim, int partition_size, int num_partitions,
+                         hipStream_t stream);
+
+int launch_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* block_tables, const int32_t* cu_seqlens,
+                   const int32_t* prefix_lens, int num_seqs, int total_q, int max_q_len,
+                   int num_q_heads, int num_kv_heads, int head_dim, int64_t num_blocks,
+                   int max_blocks_per_seq, float scale, hipStream_t stream);
+
+}  // namespace pa

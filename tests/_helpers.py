@@ -79,6 +79,7 @@ def bf16_tolerance_report(gpu_f64: np.ndarray, ref_f64: np.ndarray, atol=4e-3):
         "max_abs": float(err.max()) if err.size else 0.0,
         "mean_abs": float(err.mean()) if err.size else 0.0,
         "floor_max_abs": float(floor.max()) if floor.size else 0.0,
+        "floor_mean_abs": float(floor.mean()) if floor.size else 0.0,
         "n_fail": int(np.count_nonzero(~(ok_abs | ok_ulp))),
         "n_ulp_only": int(np.count_nonzero(ok_ulp & ~ok_abs)),
         "n_nonfinite": int(np.count_nonzero(~np.isfinite(gpu_f64))),

@@ -1,0 +1,191 @@
+"""C-ABI contract on the CPU: the library loads, exports every function the
+header declares, and rejects invalid arguments on the host before any HIP
+call (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_gqa_write_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+INVALID, UNSUPPORTED, OK = pa.PA_ERR_INVALID_ARG, pa.PA_ERR_UNSUPPORTED, pa.PA_OK
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def header_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(pa_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return pa.load_library()
+
+
+def test_header_declares_the_boundary():
+    assert header_functions() == sorted(["pa_write_kv", "pa_decode", "pa_decode_reduce",
+                                         "pa_prefill", "pa_decode_split_plan",
+                                         "pa_status_string"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert set(header_functions()) == set(pa.EXPORTED_SYMBOLS)
+
+
+def test_exported_symbols_have_c_linkage():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", pa.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    names = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    for name in header_functions():
+        assert name in names, name
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="no fallback"):
+        pa.load_library(str(tmp_path / "nope.so"))
+
+
+def test_status_strings(lib):
+    for code in (OK, INVALID, UNSUPPORTED, pa.PA_ERR_LAUNCH):
+        s = lib.pa_status_string(code).decode()
+        assert s.startswith("PA_")
+    assert "unknown" in lib.pa_status_string(7).decode()
+
+
+def _write(lib, **kw):
+    a = dict(k_new=FAKE, v_new=FAKE, slots=FAKE, kc=FAKE, vc=FAKE, T=4, hkv=8, d=128, bs=16,
+             nb=64)
+    a.update(kw)
+    return lib.pa_write_kv(a["k_new"], a["v_new"], a["slots"], a["kc"], a["vc"], a["T"],
+                           a["hkv"], a["d"], a["bs"], a["nb"], None)
+
+
+def test_write_kv_validation(lib):
+    assert _write(lib, T=-1) == INVALID
+    assert _write(lib, hkv=0) == INVALID
+    assert _write(lib, nb=-5) == INVALID
+    assert _write(lib, d=96) == UNSUPPORTED
+    assert _write(lib, bs=32) == UNSUPPORTED
+    assert _write(lib, k_new=None) == INVALID
+    assert _write(lib, slots=None) == INVALID
+    assert _write(lib, vc=None) == INVALID
+    # zero tokens is a no-op that touches nothing (null pointers allowed)
+    assert _write(lib, T=0, k_new=None, v_new=None, slots=None, kc=None, vc=None) == OK
+
+
+def _decode(lib, **kw):
+    a = dict(out=FAKE, po=FAKE, pl=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, ctx=FAKE, B=8,
+             hq=32, hkv=8, d=128, bs=16, nb=4096, mb=72, ps=256, P=5, scale=0.088)
+    a.update(kw)
+    return lib.pa_decode(a["out"], a["po"], a["pl"], a["q"], a["kc"], a["vc"], a["bt"], a["ctx"],
+                         a["B"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["mb"], a["ps"],
+                         a["P"], a["scale"], None)
+
+
+def test_decode_validation(lib):
+    assert _decode(lib, B=-1) == INVALID
+    assert _decode(lib, hq=30) == INVALID           # not a multiple of Hkv
+    assert _decode(lib, hq=0) == INVALID
+    assert _decode(lib, hq=136, hkv=4) == UNSUPPORTED  # group 34 > 16
+    assert _decode(lib, d=80) == UNSUPPORTED
+    assert _decode(lib, bs=8) == UNSUPPORTED
+    assert _decode(lib, mb=0) == INVALID
+    assert _decode(lib, ps=100) == INVALID          # not a multiple of 16
+    assert _decode(lib, ps=0) == INVALID
+    assert _decode(lib, P=0) == INVALID
+    assert _decode(lib, scale=float("nan")) == INVALID
+    assert _decode(lib, scale=float("inf")) == INVALID
+    assert _decode(lib, q=None) == INVALID
+    assert _decode(lib, bt=None) == INVALID
+    assert _decode(lib, ctx=None) == INVALID
+    assert _decode(lib, P=1, out=None) == INVALID
+    assert _decode(lib, P=4, po=None) == INVALID
+    assert _decode(lib, P=4, pl=None) == INVALID
+    assert _decode(lib, P=0x40000000, hkv=8, B=8) == UNSUPPORTED  # grid too large
+    assert _decode(lib, B=0, q=None, kc=None, vc=None, bt=None, ctx=None, out=None) == OK
+
+
+def _reduce(lib, **kw):
+    a = dict(out=FAKE, po=FAKE, pl=FAKE, ctx=FAKE, B=8, hq=32, d=128, ps=256, P=5)
+    a.update(kw)
+    return lib.pa_decode_reduce(a["out"], a["po"], a["pl"], a["ctx"], a["B"], a["hq"], a["d"],
+                                a["ps"], a["P"], None)
+
+
+def test_reduce_validation(lib):
+    assert _reduce(lib, B=-2) == INVALID
+    assert _reduce(lib, hq=0) == INVALID
+    assert _reduce(lib, d=32) == UNSUPPORTED
+    assert _reduce(lib, ps=24) == INVALID
+    assert _reduce(lib, P=0) == INVALID
+    assert _reduce(lib, out=None) == INVALID
+    assert _reduce(lib, po=None) == INVALID
+    assert _reduce(lib, pl=None) == INVALID
+    assert _reduce(lib, B=0, out=None, po=None, pl=None) == OK
+
+
+def _prefill(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cu=FAKE, pre=FAKE, S=4, tq=4096,
+             mq=1024, hq=32, hkv=8, d=128, bs=16, nb=4096, mb=96, scale=0.088)
+    a.update(kw)
+    return lib.pa_prefill(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["cu"], a["pre"], a["S"],
+                          a["tq"], a["mq"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["mb"],
+                          a["scale"], None)
+
+
+def test_prefill_validation(lib):
+    assert _prefill(lib, S=-1) == INVALID
+    assert _prefill(lib, tq=-1) == INVALID
+    assert _prefill(lib, mq=-1) == INVALID
+    assert _prefill(lib, hq=33) == INVALID
+    assert _prefill(lib, d=512) == UNSUPPORTED
+    assert _prefill(lib, bs=64) == UNSUPPORTED
+    assert _prefill(lib, mb=0) == INVALID
+    assert _prefill(lib, scale=float("nan")) == INVALID
+    assert _prefill(lib, cu=None) == INVALID
+    assert _prefill(lib, out=None) == INVALID
+    assert _prefill(lib, S=0) == OK
+    assert _prefill(lib, tq=0, q=None, out=None) == OK
+
+
+def plan(lib, B, hkv, ctx, cus=256):
+    ps, npart = ctypes.c_int32(), ctypes.c_int32()
+    st = lib.pa_decode_split_plan(B, hkv, ctx, cus, ctypes.byref(ps), ctypes.byref(npart))
+    return st, ps.value, npart.value
+
+
+@pytest.mark.parametrize("B,hkv,ctx", [(8, 8, 1152), (64, 8, 1152), (4, 8, 8192), (8, 2, 8192),
+                                       (2, 2, 50), (1, 1, 1), (1, 1, 0), (300, 8, 100000)])
+def test_split_plan_covers_context(lib, B, hkv, ctx):
+    st, ps, npart = plan(lib, B, hkv, ctx)
+    assert st == OK
+    assert ps > 0 and ps % 16 == 0 and npart >= 1
+    assert ps * npart >= max(ctx, 1)
+    if npart > 1:
+        assert ps % 128 == 0
+        assert ps * (npart - 1) < ctx        # no partition is empty at max context
+
+
+def test_split_plan_fills_the_gpu(lib):
+    # small batches get split so that there are at least ~2 workgroups per CU
+    st, ps, npart = plan(lib, 4, 8, 8192)
+    assert 4 * 8 * npart >= 2 * 256 * 0.5
+    st, ps, npart = plan(lib, 64, 8, 1152)
+    assert npart == 1                       # 512 items already fill 256 CUs twice
+
+
+def test_split_plan_validation(lib):
+    ps, npart = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.pa_decode_split_plan(1, 1, 10, 256, None, ctypes.byref(npart)) == INVALID
+    assert lib.pa_decode_split_plan(-1, 1, 10, 256, ctypes.byref(ps), ctypes.byref(npart)) == INVALID
+    assert lib.pa_decode_split_plan(1, 0, 10, 256, ctypes.byref(ps), ctypes.byref(npart)) == INVALID
+    assert lib.pa_decode_split_plan(1, 1, 10, 0, ctypes.byref(ps), ctypes.byref(npart)) == INVALID

@@ -1,0 +1,109 @@
+"""pa_prefill on the GPU against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from _gpu_helpers import (announce, check_tolerance, decode_gpu, prefill_gpu, prefill_oracle,
+                          prefill_oracle_pools)
+from _helpers import bits
+
+pytestmark = pytest.mark.gpu
+
+
+def test_prefill_qwen3_4b_full_parity():
+    """4 x 1024 new tokens, two of them after 512 cached tokens: every output
+    element against the oracle.  The literal 4e-3 max is below the bf16
+    rounding floor of this case's short rows, so the per-element bar is
+    '<= 4e-3 or a bf16 neighbour of the exact value'."""
+    announce("prefill qwen3_4b_prefill_4x1024")
+    case = workloads.qwen3_4b_prefill()
+    out = prefill_gpu(case)
+    check_tolerance("qwen3_4b prefill", out, prefill_oracle(case), literal=False)
+
+
+def _sampled_rows(n):
+    rows = list(range(0, 64)) + list(range(n // 2 - 8, n // 2 + 8)) + list(range(n - 40, n))
+    return sorted(set(r for r in rows if 0 <= r < n))
+
+
+def test_prefill_hybrid_4097_sampled_parity():
+    """One 4097-token prefill at head_dim 256: sampled rows, each computed by
+    the oracle as a decode of that token over its causal context (the oracle
+    invariant 'prefill row i = decode with context prefix+i+1')."""
+    announce("prefill hybrid_prefill_4097")
+    case = workloads.hybrid_prefill()
+    out = prefill_gpu(case)
+    kc, vc = prefill_oracle_pools(case)
+    rows = _sampled_rows(case.total_q)
+    q = bits(case.q)
+    ref = np.stack([oracle.decode(q[r:r + 1], kc, vc, case.block_tables.numpy()[:1], [r + 1],
+                                  case.scale, case.num_q_heads, case.num_kv_heads)[0]
+                    for r in rows])
+    check_tolerance("hybrid prefill sampled", out[rows], ref, literal=False)
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(4, 2, 64), (8, 8, 128), (32, 8, 128), (12, 4, 128),
+                                      (16, 2, 256), (6, 1, 256), (16, 1, 64)])
+def test_prefill_ragged_with_prefixes(hq, hkv, d):
+    announce(f"prefill ragged hq={hq} hkv={hkv} d={d}")
+    case = workloads.make_prefill_case("ragged", q_lens=[1, 15, 17, 100, 300],
+                                       prefix_lens=[0, 1, 17, 500, 33], num_q_heads=hq,
+                                       num_kv_heads=hkv, head_dim=d, num_blocks=128,
+                                       seed=hq * 100 + d)
+    out = prefill_gpu(case)
+    check_tolerance(f"ragged {hq}/{hkv}/{d}", out, prefill_oracle(case), literal=False)
+
+
+def test_prefill_empty_sequences_and_single_tokens():
+    announce("prefill empty/single")
+    case = workloads.make_prefill_case("empty", q_lens=[0, 1, 0, 3], prefix_lens=[5, 0, 0, 16],
+                                       num_q_heads=8, num_kv_heads=2, head_dim=128,
+                                       num_blocks=16, seed=5)
+    out = prefill_gpu(case)
+    check_tolerance("empty/single", out, prefill_oracle(case))
+
+
+def test_prefill_bad_table_entry_poisons_only_its_sequence():
+    announce("prefill bad table entry")
+    case = workloads.make_prefill_case("bad", q_lens=[40, 40], prefix_lens=[16, 16],
+                                       num_q_heads=8, num_kv_heads=2, head_dim=128,
+                                       num_blocks=16, seed=8)
+    ref = prefill_oracle(case)
+    # corrupt sequence 1's first (prefix) block id after its new tokens were written
+    import paged_kv_gqa_write_amd as pa
+    from _gpu_helpers import DEV
+    kc, vc = case.k_cache.to(DEV), case.v_cache.to(DEV)
+    pa.write_kv(case.k_new.to(DEV), case.v_new.to(DEV), case.slot_mapping.to(DEV), kc, vc)
+    bt = case.block_tables.clone()
+    bt[1, 0] = 99
+    out = pa.prefill(case.q.to(DEV), kc, vc, bt.to(DEV), case.cu_seqlens.to(DEV),
+                     case.prefix_lens.to(DEV), case.scale, 40).cpu()
+    assert torch.isnan(out[40:].float()).all()
+    check_tolerance("bad entry, good sequence", out[:40], ref[:40])
+
+
+def test_prefill_last_row_matches_gpu_decode():
+    announce("prefill vs decode")
+    case = workloads.make_prefill_case("pd", q_lens=[200], prefix_lens=[77], num_q_heads=32,
+                                       num_kv_heads=8, head_dim=128, num_blocks=32, seed=3)
+    out = prefill_gpu(case)
+    dcase = workloads.make_decode_case("pd", context_lens=[277], num_q_heads=32, num_kv_heads=8,
+                                       head_dim=128, num_blocks=32, seed=3, poison=False)
+    kc, vc = prefill_oracle_pools(case)
+    from _helpers import from_bits
+    dcase.k_cache, dcase.v_cache = from_bits(kc), from_bits(vc)
+    dcase.block_tables = case.block_tables.clone()
+    dcase.q = case.q[-1:].clone()
+    dout = decode_gpu(dcase, write_new=False)
+    diff = (dout[0].float() - out[-1].float()).abs().max().item()
+    assert diff <= 8e-3, diff
+
+
+def test_prefill_repeat_runs_bitwise_identical():
+    announce("prefill determinism")
+    case = workloads.make_prefill_case("det", q_lens=[300, 129], prefix_lens=[64, 0],
+                                       num_q_heads=32, num_kv_heads=8, head_dim=128,
+                                       num_blocks=64, seed=10)
+    assert torch.equal(prefill_gpu(case), prefill_gpu(case))
