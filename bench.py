@@ -15,7 +15,8 @@ sequences after 512 cached tokens) over the same 36-layer stack.
 
 Prints ONE JSON line.  `value` = whole-step KV bytes / step time.  The
 roofline object covers the decode kernel: algorithmic KV bytes per launch /
-its average launch duration measured with HIP events on the launch stream.
+its average launch duration (the step's decode launches re-issued back to
+back between HIP events on the launch stream).
 cpu_baseline = the CPU fp64 oracle timed on a bounded sample of the same
 workload.
 """
@@ -139,26 +140,23 @@ def main():
     kv_bytes_layer = case.kv_bytes()
     value = kv_bytes_layer * L / (ms_step * 1e-3) / 1e9
 
-    # Decode kernel alone: HIP events around every pa_decode launch over the
-    # same K steps (pa_write_kv and the reduce run outside the brackets).
-    evs = []
+    # Decode kernel alone: the same K steps' pa_decode launches issued back to
+    # back on the launch stream between one pair of HIP events (pa_write_kv
+    # and the reduce are left out), so the average is the kernel's own
+    # duration plus the hardware's inter-dispatch gap -- what rocprofv3's
+    # kernel trace reports for it, without per-launch event overhead.
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
     for _ in range(args.steps):
         for i in range(L):
-            lib.pa_write_kv(k_new.data_ptr(), v_new.data_ptr(), slots.data_ptr(),
-                            kc[i].data_ptr(), vc[i].data_ptr(), B, hkv, d, 16, nb, sptr)
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
             lib.pa_decode(out.data_ptr(), part_out.data_ptr(), part_lse.data_ptr(), q.data_ptr(),
                           kc[i].data_ptr(), vc[i].data_ptr(), bt.data_ptr(), ctx.data_ptr(), B,
                           hq, hkv, d, 16, nb, bt.shape[1], ps, npart, case.scale, sptr)
-            b.record(stream)
-            evs.append((a, b))
-            if npart > 1:
-                lib.pa_decode_reduce(out.data_ptr(), part_out.data_ptr(), part_lse.data_ptr(),
-                                     ctx.data_ptr(), B, hq, d, ps, npart, sptr)
+    b.record(stream)
     torch.cuda.synchronize()
-    dec_us = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e3
+    dec_us = a.elapsed_time(b) / (args.steps * L) * 1e3
     dec_gbps = kv_bytes_layer / (dec_us * 1e-6) / 1e9
     traffic = measured_traffic("decode_kernel_traffic.json", ["decode.hip", "pa_device.h"])
     roofline = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
@@ -216,18 +214,14 @@ def main():
         T, phq, phkv, pd = pc.total_q, pc.num_q_heads, pc.num_kv_heads, pc.head_dim
         maxq = max(pc.q_lens)
 
-        def prefill_layer(i, evpair=None):
+        def prefill_layer(i):
             st = lib.pa_write_kv(pkn.data_ptr(), pvn.data_ptr(), pslots.data_ptr(),
                                  pkc[i].data_ptr(), pvc[i].data_ptr(), T, phkv, pd, 16,
                                  pc.num_blocks, sptr)
-            if evpair is not None:
-                evpair[0].record(stream)
             st |= lib.pa_prefill(pout.data_ptr(), pq.data_ptr(), pkc[i].data_ptr(),
                                  pvc[i].data_ptr(), pbt.data_ptr(), pcu.data_ptr(),
                                  ppre.data_ptr(), pc.num_seqs, T, maxq, phq, phkv, pd, 16,
                                  pc.num_blocks, pbt.shape[1], pc.scale, sptr)
-            if evpair is not None:
-                evpair[1].record(stream)
             if st != 0:
                 raise RuntimeError("prefill launch failed")
 
@@ -243,14 +237,18 @@ def main():
         torch.cuda.synchronize()
         pms = t0.elapsed_time(t1) / args.steps
         flops = pc.flops()
-        pevs = []
+        # prefill kernel alone, back to back over the layers (see decode above)
+        torch.cuda.synchronize()
+        t0.record(stream)
         for _ in range(args.steps):
             for i in range(L):
-                pair = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                prefill_layer(i, pair)
-                pevs.append(pair)
+                st = lib.pa_prefill(pout.data_ptr(), pq.data_ptr(), pkc[i].data_ptr(),
+                                    pvc[i].data_ptr(), pbt.data_ptr(), pcu.data_ptr(),
+                                    ppre.data_ptr(), pc.num_seqs, T, maxq, phq, phkv, pd, 16,
+                                    pc.num_blocks, pbt.shape[1], pc.scale, sptr)
+        t1.record(stream)
         torch.cuda.synchronize()
-        pf_us = sum(a.elapsed_time(b) for a, b in pevs) / len(pevs) * 1e3
+        pf_us = t0.elapsed_time(t1) / (args.steps * L) * 1e3
         pf_tflops = flops / (pf_us * 1e-6) / 1e12
         result["prefill"] = {
             "workload": "qwen3_4b_prefill_4x1024: 4 x 1024 new tokens, sequences 1 and 3 after "

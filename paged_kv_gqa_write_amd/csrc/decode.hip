@@ -3,8 +3,11 @@
 //
 // Work decomposition: one workgroup per (partition p, KV head g, sequence s),
 // NW waves per workgroup.  The partition's KV blocks are taken two at a time
-// ("pairs", 32 keys); wave w handles pairs w, w+NW, ...  All G query heads of
-// the KV head are processed together, so each K/V byte is read once.
+// ("pairs", 32 keys); wave w handles a contiguous range of pairs.  All G
+// query heads of the KV head are processed together, so each K/V byte is read
+// once.  A wave fetches the block-table entries of up to 32 pairs with one
+// load (lane i holds entry i; pairs read them back with readlane) and keeps
+// NBUF pairs of K/V loads in flight in a ring of register buffers.
 //
 // Both contractions run on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16),
 // with the query heads as the 16-wide N dimension (zero-padded when G < 16):
@@ -16,7 +19,7 @@
 // of the pair's 32 keys such that lane group c ends up holding 8 consecutive
 // keys of one block, which is also what one 16-byte load of a V^T row gives.
 // K and V bytes go from HBM straight into MFMA operand registers with 16-byte
-// loads; the next pair's loads are issued before the current pair is used.
+// loads.
 //
 // Softmax is online (running max m, running sum l per head, base-2
 // exponentials with scale*log2(e) folded in); m is made uniform across the
@@ -41,38 +44,34 @@ struct PairRegs {
   u32x4 v[D / 16];     // D/16 d-tiles (A operand of O^T)
 };
 
-// Issue the loads of pair j (blocks x, x+1 of the sequence).  Lanes whose
-// block does not exist or is unusable get zeros; their keys are masked.
+// Issue the loads of a pair (physical blocks x, y).  Every lane loads
+// unconditionally from a valid block (a missing y block is replaced by x):
+// keys past the partition's valid range are masked out of the scores and
+// their V values are zeroed in compute_pair, so what such lanes read never
+// matters, and straight-line loads keep the whole ring of pairs in flight.
 template <int D>
 __device__ __forceinline__ void load_pair(PairRegs<D>& r, const uint16_t* __restrict__ k_cache,
                                           const uint16_t* __restrict__ v_cache, int64_t physx,
-                                          bool okx, int64_t physy, bool oky, int g, int hkv,
-                                          int col, int c) {
+                                          int64_t physy, int g, int hkv, int col, int c) {
   // K: score-tile row `col` -> key: group gr = col/4 picks the block (gr >= 2
   // -> second block) and the 4-key run 8*(gr&1) (+4 for the second tile).
   {
     const int gr = col >> 2;
-    const bool sel_y = gr >= 2;
     const int key = 8 * (gr & 1) + (col & 3);
-    const bool ok = sel_y ? oky : okx;
-    const int64_t phys = sel_y ? physy : physx;
+    const int64_t phys = gr >= 2 ? physy : physx;
     const uint16_t* base = k_cache + ((phys * hkv + g) * kBlock + key) * D + 8 * c;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int i = 0; i < D / 32; ++i)
-        r.k[t][i] = ok ? load16_stream(base + t * 4 * D + 32 * i) : u32x4{0, 0, 0, 0};
+      for (int i = 0; i < D / 32; ++i) r.k[t][i] = load16_stream(base + t * 4 * D + 32 * i);
   }
   // V^T: lane group c reads keys 8*(c&1)..+8 of block (c >= 2 ? y : x), for
   // d row 16*dt + col.
   {
-    const bool sel_y = c >= 2;
-    const bool ok = sel_y ? oky : okx;
-    const int64_t phys = sel_y ? physy : physx;
+    const int64_t phys = c >= 2 ? physy : physx;
     const uint16_t* base = v_cache + ((phys * hkv + g) * D + col) * kBlock + 8 * (c & 1);
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-      r.v[dt] = ok ? load16_stream(base + dt * 16 * kBlock) : u32x4{0, 0, 0, 0};
+    for (int dt = 0; dt < D / 16; ++dt) r.v[dt] = load16_stream(base + dt * 16 * kBlock);
   }
 }
 
@@ -136,20 +135,7 @@ __device__ __forceinline__ void compute_pair(PairRegs<D>& r, const u32x4 (&qf)[D
   }
 }
 
-// Physical blocks of pair j; flags a table entry outside the pool.
-__device__ __forceinline__ void pair_blocks(const int32_t* __restrict__ bt, int pb0, int pb1,
-                                            int j, int64_t num_blocks, int64_t& px, bool& okx,
-                                            int64_t& py, bool& oky, bool& bad) {
-  const int bx = pb0 + 2 * j;
-  px = bt[bx];
-  okx = px >= 0 && px < num_blocks;
-  const bool hy = bx + 1 < pb1;
-  py = hy ? (int64_t)bt[bx + 1] : 0;
-  oky = hy && py >= 0 && py < num_blocks;
-  bad |= !okx || (hy && !oky);
-}
-
-template <int D, int NW, bool PREFETCH>
+template <int D, int NW, int NBUF>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(
     uint16_t* __restrict__ out, float* __restrict__ part_out, float* __restrict__ part_lse,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
@@ -168,21 +154,44 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
   const int col = lane & 15;
   const int c = lane >> 4;
 
-  const int ctx = context_lens[s];
-  const int nblk = ctx > 0 ? (ctx + kBlock - 1) / kBlock : 0;
-  bool bad = ctx < 0 || nblk > max_blocks ||
-             (int64_t)ctx > (int64_t)num_partitions * blocks_per_part * kBlock;
+  // Wave w takes the contiguous pair range [k0, k0+nk) of the partition.
+  // The range comes from the partition size alone, so the block-table entries
+  // can be fetched at the same time as the context length (it only trims the
+  // range afterwards): the kernel starts with one round of independent loads.
   const int pb0 = p * blocks_per_part;
+  const int full_pairs = (blocks_per_part + 1) / 2;
+  const int k0 = (full_pairs * wave) / NW;
+  const int wb0 = pb0 + 2 * k0;  // first block of this wave
+  const int32_t* bt = block_tables + (int64_t)s * max_blocks;
+  // Block-table entries of this wave's pairs, 32 pairs (64 entries) at a
+  // time: lane i holds entry wb0 + 64*chunk + i; pair k reads lanes 2k, 2k+1.
+  int ent = 0;
+  auto load_entries = [&](int chunk) {
+    const int b = wb0 + 64 * chunk + lane;
+    ent = bt[min(b, max_blocks - 1)];
+  };
+  load_entries(0);
+
+  const int ctx = context_lens[s];
+  const int nblk = ctx > 0 ? (int)(((int64_t)ctx + kBlock - 1) / kBlock) : 0;
+  bool bad = ctx < 0 || nblk > max_blocks ||
+             (int64_t)ctx > (int64_t)num_partitions * blocks_per_part * kBlock ||
+             (nblk > 0 && num_blocks <= 0);
   const int pb1 = bad ? pb0 : min(pb0 + blocks_per_part, nblk);
   const int limit = min(ctx, pb1 * kBlock);
   const int npairs = pb1 > pb0 ? (pb1 - pb0 + 1) / 2 : 0;
+  const int k1 = min((full_pairs * (wave + 1)) / NW, npairs);
+  const int nk = max(k1 - k0, 0);
 
+  // Q of head col of the group.  Columns past the group read head 0 instead:
+  // each column's softmax is independent and those columns are never
+  // written, so their values do not matter.
   u32x4 qf[KS];
   {
-    const bool has = col < group;
-    const uint16_t* qb = q + ((int64_t)s * num_q_heads + (int64_t)g * group + col) * D + 8 * c;
+    const uint16_t* qb = q + ((int64_t)s * num_q_heads + (int64_t)g * group +
+                              (col < group ? col : 0)) * D + 8 * c;
 #pragma unroll
-    for (int i = 0; i < KS; ++i) qf[i] = has ? load16(qb + 32 * i) : u32x4{0, 0, 0, 0};
+    for (int i = 0; i < KS; ++i) qf[i] = load16(qb + 32 * i);
   }
 
   f32x4 acc[DT];
@@ -190,43 +199,41 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0, 0, 0, 0};
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int32_t* bt = block_tables + (int64_t)s * max_blocks;
   // Lane group c's keys start at block (c >= 2 ? y : x), offset 8*(c&1).
   const int lane_key0 = ((c >= 2) ? kBlock : 0) + 8 * (c & 1);
-  int64_t px, py;
-  bool okx, oky;
 
-  if (PREFETCH) {
-    // Two register sets used alternately: the loads of the next pair are in
-    // flight while the current one is consumed.
-    PairRegs<D> ra, rb;
-    int j = wave;
-    if (j < npairs) {
-      pair_blocks(bt, pb0, pb1, j, num_blocks, px, okx, py, oky, bad);
-      load_pair<D>(ra, k_cache, v_cache, px, okx, py, oky, g, num_kv_heads, col, c);
-    }
-    for (; j < npairs; j += 2 * NW) {
-      if (j + NW < npairs) {
-        pair_blocks(bt, pb0, pb1, j + NW, num_blocks, px, okx, py, oky, bad);
-        load_pair<D>(rb, k_cache, v_cache, px, okx, py, oky, g, num_kv_heads, col, c);
+  // Issue the loads of this wave's pair k into `r`.  An entry outside the
+  // pool marks the sequence bad (NaN output) and is replaced by block 0 so
+  // the loads stay in bounds (num_blocks == 0 never gets here: see above).
+  auto issue = [&](int k, PairRegs<D>& r) {
+    if ((k & 31) == 0 && k > 0) load_entries(k >> 5);
+    const int e = 2 * (k & 31);
+    int64_t px = __builtin_amdgcn_readlane(ent, e);
+    int64_t py = __builtin_amdgcn_readlane(ent, e + 1);
+    const bool hy = wb0 + 2 * k + 1 < pb1;
+    const bool okx = px >= 0 && px < num_blocks;
+    const bool oky = py >= 0 && py < num_blocks;
+    bad |= !okx || (hy && !oky);
+    px = okx ? px : 0;
+    py = (hy && oky) ? py : px;
+    load_pair<D>(r, k_cache, v_cache, px, py, g, num_kv_heads, col, c);
+  };
+
+  // Ring of NBUF register buffers: NBUF pairs are in flight while one is
+  // consumed; buffer b always holds pairs b, b+NBUF, b+2*NBUF, ...
+  PairRegs<D> buf[NBUF];
+#pragma unroll
+  for (int b = 0; b < NBUF; ++b)
+    if (b < nk) issue(b, buf[b]);
+  for (int kb = 0; kb < nk; kb += NBUF) {
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) {
+      const int k = kb + b;
+      if (k < nk) {
+        compute_pair<D>(buf[b], qf, acc, m_run, l_run, (wb0 + 2 * k) * kBlock + lane_key0, limit,
+                        scale_log2);
+        if (k + NBUF < nk) issue(k + NBUF, buf[b]);
       }
-      compute_pair<D>(ra, qf, acc, m_run, l_run, (pb0 + 2 * j) * kBlock + lane_key0, limit,
-                      scale_log2);
-      if (j + NW >= npairs) break;
-      if (j + 2 * NW < npairs) {
-        pair_blocks(bt, pb0, pb1, j + 2 * NW, num_blocks, px, okx, py, oky, bad);
-        load_pair<D>(ra, k_cache, v_cache, px, okx, py, oky, g, num_kv_heads, col, c);
-      }
-      compute_pair<D>(rb, qf, acc, m_run, l_run, (pb0 + 2 * (j + NW)) * kBlock + lane_key0,
-                      limit, scale_log2);
-    }
-  } else {
-    for (int j = wave; j < npairs; j += NW) {
-      PairRegs<D> ra;
-      pair_blocks(bt, pb0, pb1, j, num_blocks, px, okx, py, oky, bad);
-      load_pair<D>(ra, k_cache, v_cache, px, okx, py, oky, g, num_kv_heads, col, c);
-      compute_pair<D>(ra, qf, acc, m_run, l_run, (pb0 + 2 * j) * kBlock + lane_key0, limit,
-                      scale_log2);
     }
   }
 
@@ -304,7 +311,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
   }
 }
 
-// One wave per (sequence, query head).
+// One wave per (sequence, query head).  Lane p holds partition p's LSE (64
+// partitions per chunk), so the max and the weights take one load; weights
+// are broadcast with readlane and each lane accumulates its D/64 elements.
 template <int D>
 __global__ __launch_bounds__(64) void decode_reduce_kernel(
     uint16_t* __restrict__ out, const float* __restrict__ part_out,
@@ -317,13 +326,14 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(
   int np = num_partitions;
   if (context_lens != nullptr) {
     const int ctx = context_lens[s];
-    np = ctx <= 0 ? 0 : min(num_partitions, (ctx + partition_size - 1) / partition_size);
+    np = ctx <= 0 ? 0 : (int)min((int64_t)num_partitions,
+                                 ((int64_t)ctx + partition_size - 1) / partition_size);
   }
   const float* lse = part_lse + row * num_partitions;
   float M = -INFINITY;
   bool nan_seen = false;
-  for (int p = lane; p < np; p += 64) {
-    const float v = lse[p];
+  for (int p0 = 0; p0 < np; p0 += 64) {
+    const float v = (p0 + lane < np) ? lse[p0 + lane] : -INFINITY;
     nan_seen |= v != v;
     M = fmaxf(M, v);
   }
@@ -337,11 +347,17 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(
   float L = 0.f;
   if (M != -INFINITY) {
     const float* po = part_out + row * num_partitions * D + lane * EPT;
-    for (int p = 0; p < np; ++p) {
-      const float w = fast_exp2((lse[p] - M) * kLog2e);
-      L += w;
+    for (int p0 = 0; p0 < np; p0 += 64) {
+      const float w = (p0 + lane < np) ? fast_exp2((lse[p0 + lane] - M) * kLog2e) : 0.f;
+      const int cnt = min(64, np - p0);
+#pragma unroll 4
+      for (int j = 0; j < cnt; ++j) {
+        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
+        L += wj;
+        const float* src = po + (int64_t)(p0 + j) * D;
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) o[e] += w * po[(int64_t)p * D + e];
+        for (int e = 0; e < EPT; ++e) o[e] += wj * src[e];
+      }
     }
   }
   uint16_t* dst = out + row * D + lane * EPT;
@@ -373,9 +389,9 @@ int launch_decode(void* out, float* part_out, float* part_lse, const void* q,
                        num_partitions, scale_log2);
   };
   switch (head_dim) {
-    case 64: go(decode_kernel<64, NW, true>); break;
-    case 128: go(decode_kernel<128, NW, true>); break;
-    case 256: go(decode_kernel<256, NW, false>); break;
+    case 64: go(decode_kernel<64, NW, 4>); break;
+    case 128: go(decode_kernel<128, NW, 1>); break;
+    case 256: go(decode_kernel<256, NW, 2>); break;
     default: return -2;
   }
   return hipGetLastError() == hipSuccess ? 0 : -3;

@@ -5,7 +5,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "../../include/pa.h"
+#include "pa.h"
 #include "pa_launch.h"
 
 namespace {
@@ -105,17 +105,21 @@ int pa_decode_split_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t max_con
   if (!partition_size || !num_partitions) return PA_ERR_INVALID_ARG;
   if (num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0 || num_compute_units <= 0)
     return PA_ERR_INVALID_ARG;
-  // Aim for at least two workgroups per compute unit.  A partition is a
-  // multiple of 128 tokens (one 32-key pair for each of the 4 waves of a
-  // workgroup), so every wave of a workgroup gets the same number of pairs.
-  constexpr int64_t kUnit = 128;
+  // The decode kernel runs one 4-wave workgroup per compute unit, so aim for
+  // one workgroup per CU: split each (sequence, KV head) into enough
+  // partitions, but never below 4 pairs of blocks (one 32-key pair per wave).
+  // Partitions are whole pairs (multiples of 32 tokens); the waves of a
+  // workgroup split a partition's pairs evenly.
+  constexpr int64_t kPair = 32;
+  constexpr int64_t kMinPart = 4 * kPair;
   const int64_t items = (int64_t)num_seqs * num_kv_heads;
   const int64_t ctx = max_context_len > 0 ? max_context_len : 1;
-  const int64_t want = 2LL * num_compute_units;
-  int64_t parts = items > 0 ? (want + items - 1) / items : 1;
+  int64_t parts = items > 0 ? (num_compute_units + items - 1) / items : 1;
+  const int64_t max_parts = (ctx + kMinPart - 1) / kMinPart;
+  if (parts > max_parts) parts = max_parts;
   if (parts < 1) parts = 1;
   int64_t ps = (ctx + parts - 1) / parts;
-  ps = ((ps + kUnit - 1) / kUnit) * kUnit;
+  ps = ((ps + kPair - 1) / kPair) * kPair;
   int64_t np = (ctx + ps - 1) / ps;
   if (np == 1) ps = ((ctx + kBlockSize - 1) / kBlockSize) * kBlockSize;
   if (ps > 0x7FFFFFF0LL) return PA_ERR_INVALID_ARG;
