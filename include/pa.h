@@ -118,7 +118,8 @@ int pa_write_kv(const void* k_new, const void* v_new, const int64_t* slot_mappin
  *   block_tables   device, int32 [num_seqs, max_blocks_per_seq]
  *   context_lens   device, int32 [num_seqs] (0 gives a zero output)
  *   partition_size multiple of 16, > 0
- *   scale          softmax scale applied to <q, k> in fp32 (e.g. 1/sqrt(D))
+ *   scale          softmax scale applied to <q, k> in fp32 (e.g. 1/sqrt(D));
+ *                  finite and >= 0 (a negative scale is PA_ERR_INVALID_ARG)
  */
 int pa_decode(void* out, float* part_out, float* part_lse,
               const void* q, const void* k_cache, const void* v_cache,
@@ -165,6 +166,7 @@ int pa_decode_reduce(void* out, const float* part_out, const float* part_lse,
  *   prefix_lens    device, int32 [num_seqs], or NULL for no cached prefixes
  *   max_q_len      host upper bound of n_s (sizes the launch grid; rows of
  *                  a sequence beyond it are not written)
+ *   scale          as for pa_decode (finite, >= 0)
  */
 int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
                const int32_t* block_tables, const int32_t* cu_seqlens,

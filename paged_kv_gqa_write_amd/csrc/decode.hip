@@ -150,7 +150,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
   const int g = (wg / num_partitions) % num_kv_heads;
   const int s = wg / (num_partitions * num_kv_heads);
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int col = lane & 15;
   const int c = lane >> 4;
 

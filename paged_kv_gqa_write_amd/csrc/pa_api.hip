@@ -54,7 +54,7 @@ int pa_decode(void* out, float* part_out, float* part_lse, const void* q, const 
   if (max_blocks_per_seq <= 0) return PA_ERR_INVALID_ARG;
   if (partition_size <= 0 || partition_size % kBlockSize != 0) return PA_ERR_INVALID_ARG;
   if (num_partitions < 1) return PA_ERR_INVALID_ARG;
-  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || scale < 0.f) return PA_ERR_INVALID_ARG;
   if ((int64_t)num_partitions * num_kv_heads * num_seqs > kMaxGrid) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
@@ -90,7 +90,7 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
   int st = check_heads(num_q_heads, num_kv_heads, head_dim, block_size);
   if (st != PA_OK) return st;
   if (max_blocks_per_seq <= 0) return PA_ERR_INVALID_ARG;
-  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || scale < 0.f) return PA_ERR_INVALID_ARG;
   if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !cu_seqlens)
     return PA_ERR_INVALID_ARG;

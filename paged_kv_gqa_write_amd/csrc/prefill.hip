@@ -8,18 +8,30 @@
 //
 // Work decomposition.  A workgroup of NW waves owns COLS = NW*16*NT
 // consecutive columns of one (s, g); wave w owns 16*NT of them (NT MFMA
-// column tiles).  The workgroup walks the keys 0..P_s+i_max in tiles of BK
-// keys: the tile's blocks are looked up in the block table and copied
-// (16-byte loads, next tile prefetched into registers) into LDS, K as
-// [key][d] rows and V as [d][key] rows.  Waves then run, per 32-key pair:
-//   S^T[key][col]  = K[key][:]   . Q^T[:][col]    (v_mfma_f32_16x16x32_bf16)
-//   online softmax per column (base-2, scale*log2(e) folded in)
+// column tiles, Q held in registers).  The workgroup walks the keys
+// 0..P_s+i_max in tiles of BK keys.
+//
+// Staging.  Each tile's blocks are looked up in the block table (scalar
+// loads) and copied HBM -> LDS with global_load_lds_dwordx4 (16 bytes per
+// lane, no registers involved), S tiles deep: while tile t is consumed,
+// tiles t+1..t+S-1 are in flight.  Each wave waits for its own copies with an
+// explicit vmcnt and one raw barrier per tile publishes the tile and frees
+// the buffer the next copy goes to.  A direct copy writes 1 KiB of LDS per
+// wave instruction in lane order, so the source chunk each lane fetches is
+// chosen to realise an XOR-swizzled layout in which every 16-lane group of a
+// 16-byte operand read hits 16 different bank quads (gfx950 LDS: 64 banks).
+//   K tile   [BK keys][D], row r chunk j stored at chunk j ^ kswz(r)
+//   V^T tile [BK/16 blocks][D rows][16 keys], row d half h at h ^ ((d>>3)&1)
+//
+// Math per 32-key pair (v_mfma_f32_16x16x32_bf16):
+//   S^T[key][col]  = K[key][:]   . Q^T[:][col]
+//   online softmax per column (base-2, scale*log2(e) folded into one FMA
+//   per element, lazy rescale, row sums on the matrix core)
 //   O^T[d][col]   += V^T[d][key] . P^T[key][col]
-// with the same key permutation as the decode kernel: score-tile row r of
-// the pair's two tiles holds key 8*(r/4) + r%4 (+4 for the second tile), so
-// lane group c ends up with keys 8c..8c+7 of the pair -- exactly one 16-byte
-// LDS read of a V^T row -- and P stays in registers as the B operand.
-// Each K/V fragment read from LDS feeds NT MFMAs.
+// Score-tile row r of the pair's two tiles holds key 8*(r/4) + r%4 (+4 for
+// the second tile), so lane group c ends up with keys 8c..8c+7 of the pair,
+// which is one 16-byte read of a V^T row: P stays in registers as the B
+// operand.  Each K/V fragment read from LDS feeds NT MFMAs.
 //
 // Scheduling: workgroup slots with the most keys (last columns of a
 // sequence) are dispatched first.
@@ -33,38 +45,74 @@ namespace pa {
 namespace {
 
 constexpr float kLog2e = 1.44269504088896341f;
+// Reference-max slack (log2 units) before the accumulators are rescaled.
+constexpr float kRescaleLog2 = 8.f;
 
-template <int D, int NT, int BK, int NW>
+typedef const int32_t __attribute__((address_space(4)))* const_i32_ptr;
+
+template <int D, int NT, int BK, int NW, int S>
 struct PrefillCfg {
   static constexpr int kColsWave = 16 * NT;
   static constexpr int kCols = kColsWave * NW;
-  static constexpr int kThreads = NW * 64;
-  static constexpr int kKRow = D + 8;    // LDS K row stride (elements): 16-byte pad
-  static constexpr int kVRow = BK + 8;   // LDS V^T row stride (elements)
   static constexpr int kBlocks = BK / kBlock;
-  // 16-byte chunks per tile for K (and for V): kBlocks * 16 * D / 8.
-  static constexpr int kChunks = kBlocks * 2 * D;
-  static constexpr int kChunksPerThread = kChunks / kThreads;
-  static_assert(kChunks % kThreads == 0, "tile must split evenly over threads");
+  static constexpr int kKBytes = BK * D * 2;
+  static constexpr int kVBytes = BK * D * 2;
+  static constexpr int kStageBytes = kKBytes + kVBytes;
+  static constexpr int kDmaK = kKBytes / 1024;     // 1 KiB wave copies per K tile
+  static constexpr int kDma = kStageBytes / 1024;  // ... per stage
+  static constexpr int kDmaPerWave = kDma / NW;
+  static_assert(kDmaK % NW == 0 && (kDma - kDmaK) % NW == 0,
+                "stage copies must split evenly over waves");
   static_assert(BK % 32 == 0, "tile is a whole number of 32-key pairs");
+  static_assert(S >= 2 && S <= 4, "2..4 stages");
 };
 
-template <int D, int NT, int BK, int NW>
-__global__ __launch_bounds__(NW * 64) void prefill_kernel(
+// K-tile swizzle: chunk (16 bytes) j of row r is stored at j ^ kswz(r).  For a
+// 16-lane operand read the lanes' rows are 8*(l/4) + l%4 (+ a multiple of 4),
+// and kswz maps them to 16 distinct values (D >= 128: rows are whole multiples
+// of the 256-byte bank line) or, with the row parity, to 16 distinct bank
+// quads (D = 64: two rows per bank line).
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+  if constexpr (D == 64)
+    return (((r >> 3) & 3) << 1) | ((r >> 1) & 1);
+  else
+    return (((r >> 3) & 3) << 2) | (r & 3);
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int D, int NT, int BK, int NW, int S, int WPE>
+__global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ prefix_lens, int num_seqs, int total_q, int max_q_len,
     int num_q_heads, int num_kv_heads, int group, int64_t num_blocks, int max_blocks,
     int nslots, float scale_log2) {
-  using Cfg = PrefillCfg<D, NT, BK, NW>;
+  using Cfg = PrefillCfg<D, NT, BK, NW, S>;
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
-  constexpr int KROW = Cfg::kKRow;
-  constexpr int VROW = Cfg::kVRow;
-  constexpr int CPT = Cfg::kChunksPerThread;
-  __shared__ __attribute__((aligned(16))) uint16_t sk[2][BK * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t sv[2][D * VROW];
+  constexpr int KB = Cfg::kKBytes;
+  constexpr int DPW = Cfg::kDmaPerWave;
+  // One LDS object per stage: distinct objects let the compiler see that the
+  // buffer being read is not one being filled by the copies still in flight.
+  __shared__ __attribute__((aligned(1024))) uint8_t smem0[Cfg::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem1[Cfg::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem2[S >= 3 ? Cfg::kStageBytes : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem3[S >= 4 ? Cfg::kStageBytes : 16];
+  auto stage = [&](auto st) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int I = decltype(st)::value;
+    if constexpr (I == 0) return smem0;
+    else if constexpr (I == 1) return smem1;
+    else if constexpr (I == 2) return smem2;
+    else return smem3;
+  };
 
   const int per_slot = num_seqs * num_kv_heads;
   const int bid = blockIdx.x;
@@ -81,204 +129,274 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(
   if (c0 >= ncols) return;
   const int P = prefix_lens != nullptr ? prefix_lens[s] : 0;
   const int64_t L = (int64_t)P + (q1 - q0);
-  const bool bad = P < 0 || (L + kBlock - 1) / kBlock > max_blocks;
+  const bool bad = P < 0 || (L + kBlock - 1) / kBlock > max_blocks || num_blocks <= 0;
   const int pos_max = (min(ncols, c0 + Cfg::kCols) - 1) / group;
   const int kend = bad ? 0 : P + pos_max + 1;  // keys this workgroup needs
   const int ntiles = (kend + BK - 1) / BK;
-  const int32_t* bt = block_tables + (int64_t)s * max_blocks;
+  const const_i32_ptr btc = (const_i32_ptr)(block_tables + (int64_t)s * max_blocks);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int col = lane & 15;
   const int c = lane >> 4;
 
-  // Columns of this lane: one per column tile.
-  int lim[NT];       // last visible key, -1 for a column past the sequence
+  // Columns of this lane: one per column tile.  A column past the sequence
+  // reads a valid row (its results are never written) and has limit -1.
+  int lim[NT];
   int qrow[NT], qhead[NT];
   u32x4 qf[NT][KS];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int cidx = c0 + wave * Cfg::kColsWave + 16 * nt + col;
     const bool ok = cidx < ncols;
-    const int pos = ok ? cidx / group : 0;
-    const int h = ok ? cidx - pos * group : 0;
+    const int cc = ok ? cidx : ncols - 1;
+    const int pos = cc / group;
+    const int h = cc - pos * group;
     lim[nt] = ok ? P + pos : -1;
     qrow[nt] = q0 + pos;
     qhead[nt] = g * group + h;
     const uint16_t* qb = q + ((int64_t)qrow[nt] * num_q_heads + qhead[nt]) * D + 8 * c;
 #pragma unroll
-    for (int i = 0; i < KS; ++i) qf[nt][i] = ok ? load16(qb + 32 * i) : u32x4{0, 0, 0, 0};
+    for (int i = 0; i < KS; ++i) qf[nt][i] = load16(qb + 32 * i);
   }
+  // Q (and nothing else) is in flight: settle it so that from here on the
+  // only vector-memory operations are the tile copies counted below.
+  wait_vm<0>();
+
+  int wave_min_lim = lim[0];
+#pragma unroll
+  for (int nt = 1; nt < NT; ++nt) wave_min_lim = min(wave_min_lim, lim[nt]);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) wave_min_lim = min(wave_min_lim, __shfl_xor(wave_min_lim, m, 64));
 
   f32x4 acc[NT][DT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[nt][dt] = f32x4{0, 0, 0, 0};
-  float m_run[NT], l_run[NT];
+  // Running max (log2 domain) and the running row sum.  The sum is kept by
+  // the matrix core: ONES(16x32) . P^T gives every row the column sum of P,
+  // so l_acc[nt][0] is the column's sum of the bf16 weights actually used.
+  float m_run[NT];
+  f32x4 l_acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     m_run[nt] = -INFINITY;
-    l_run[nt] = 0.f;
+    l_acc[nt] = f32x4{0, 0, 0, 0};
   }
+  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0 x 8
 
-  // ---- tile staging: global -> registers -> LDS ---------------------------
-  u32x4 rk[CPT], rv[CPT];
+  // ---- tile copies: HBM -> LDS ---------------------------------------------
+  // A wave's K copies and V copies of a tile all fall in one block of the
+  // tile (checked below), so each wave needs one table entry per tile.
+  constexpr int KPW = Cfg::kDmaK / NW;
+  constexpr int VPW = (Cfg::kDma - Cfg::kDmaK) / NW;
+  constexpr int kRowsPer = 1024 / (2 * D);  // K rows per 1 KiB copy
+  constexpr int kVPerBlock = D / 32;        // 1 KiB V^T copies per block
+  static_assert(KPW * kRowsPer <= kBlock && kBlock % (KPW * kRowsPer) == 0, "K copies of a wave share a block");
+  static_assert(VPW <= kVPerBlock && kVPerBlock % VPW == 0, "V copies of a wave share a block");
+  static_assert((KPW * kRowsPer) * kVPerBlock == kBlock * VPW, "K and V copies of a wave share the block");
+  const int wave_blk = (wave * KPW * kRowsPer) / kBlock;
   bool bad_entry = false;
-  auto fetch = [&](int tile) {
-#pragma unroll
-    for (int e = 0; e < CPT; ++e) {
-      const int ch = tid + e * Cfg::kThreads;
-      const int b = ch / (2 * D);          // block within the tile
-      const int w = ch - b * (2 * D);      // 16-byte chunk within the block tile
-      const int lblk = tile * Cfg::kBlocks + b;
-      const int kpos0 = lblk * kBlock;
-      rk[e] = u32x4{0, 0, 0, 0};
-      rv[e] = u32x4{0, 0, 0, 0};
-      if (kpos0 < kend) {
-        const int64_t phys = bt[lblk];
-        if (phys >= 0 && phys < num_blocks) {
-          const int64_t tbase = (phys * num_kv_heads + g) * (int64_t)(kBlock * D);
-          rk[e] = load16(k_cache + tbase + 8 * w);
-          u32x4 v = load16(v_cache + tbase + 8 * w);
-          // V^T chunk w holds keys 8*(w&1)..+8 of d row w/2; keys at or past
-          // kend are never weighted but may hold NaN: zero them.
-          const int key0 = kpos0 + 8 * (w & 1);
-          if (key0 + 8 > kend) {
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-              const uint32_t keep = ((key0 + 2 * x < kend) ? 0x0000FFFFu : 0u) |
-                                    ((key0 + 2 * x + 1 < kend) ? 0xFFFF0000u : 0u);
-              v[x] &= keep;
-            }
-          }
-          rv[e] = v;
-        } else {
-          bad_entry = true;
-        }
-      }
+  // Table entry of this wave's block in `tile` (block 0 stands in for blocks
+  // past the keys needed -- never weighted -- and for bad entries).
+  auto entry_of = [&](int tile) __attribute__((always_inline)) -> int64_t {
+    const int lb = tile * Cfg::kBlocks + wave_blk;
+    if (tile >= ntiles || lb * kBlock >= kend) return 0;
+    const int64_t p = btc[lb];
+    if (p < 0 || p >= num_blocks) {
+      bad_entry = true;
+      return 0;
     }
+    return p;
   };
-  auto stash = [&](int buf) {
+  auto issue = [&](int64_t phys, uint8_t* sb) __attribute__((always_inline)) {
+    const int64_t tile_base = (phys * num_kv_heads + g) * (int64_t)(kBlock * D);
 #pragma unroll
-    for (int e = 0; e < CPT; ++e) {
-      const int ch = tid + e * Cfg::kThreads;
-      const int b = ch / (2 * D);
-      const int w = ch - b * (2 * D);
-      // K chunk w: key w/(D/8), d 8*(w%(D/8)).
-      const int key = w / (D / 8);
-      const int dk = 8 * (w - key * (D / 8));
-      *reinterpret_cast<u32x4*>(&sk[buf][(b * kBlock + key) * KROW + dk]) = rk[e];
-      // V^T chunk w: d row w/2, keys 8*(w&1).
-      const int dv = w >> 1;
-      *reinterpret_cast<u32x4*>(&sv[buf][dv * VROW + b * kBlock + 8 * (w & 1)]) = rv[e];
+    for (int k = 0; k < KPW; ++k) {
+      const int m = wave * KPW + k;
+      const int r0 = m * kRowsPer;
+      const int off = 16 * lane;
+      const int r = r0 + off / (2 * D);
+      const int j = ((off % (2 * D)) / 16) ^ kswz<D>(r);
+      __builtin_amdgcn_global_load_lds(k_cache + tile_base + (r & 15) * D + 8 * j, sb + 1024 * m,
+                                       16, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < VPW; ++k) {
+      const int mv = wave * VPW + k;
+      const int d = 32 * (mv % kVPerBlock) + (lane >> 1);
+      const int h = (lane & 1) ^ ((d >> 3) & 1);
+      __builtin_amdgcn_global_load_lds(v_cache + tile_base + d * kBlock + 8 * h,
+                                       sb + KB + 1024 * mv, 16, 0, 0);
     }
   };
 
   // K row of score tile t, pair kp, for this lane: key 8*(col/4) + col%4 + 4t.
   const int krow0 = 8 * (col >> 2) + (col & 3);
 
-  if (ntiles > 0) {
-    fetch(0);
-    stash(0);
-  }
-  __syncthreads();
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int buf = tile & 1;
-    if (tile + 1 < ntiles) fetch(tile + 1);
-    const uint16_t* skb = sk[buf];
-    const uint16_t* svb = sv[buf];
-    auto run_tile = [&](auto hilo_tag) {
-      constexpr bool HILO = decltype(hilo_tag)::value;
+  auto run_tile = [&](int tile, const uint8_t* sb, auto hilo_tag) __attribute__((always_inline)) {
+    constexpr bool HILO = decltype(hilo_tag)::value;
+    const uint8_t* vb = sb + KB;
 #pragma unroll
-      for (int kp = 0; kp < BK / 32; ++kp) {
-        f32x4 s0[NT], s1[NT];
+    for (int kp = 0; kp < BK / 32; ++kp) {
+      f32x4 s0[NT], s1[NT];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          s0[nt] = f32x4{0, 0, 0, 0};
-          s1[nt] = f32x4{0, 0, 0, 0};
-        }
+      for (int nt = 0; nt < NT; ++nt) {
+        s0[nt] = f32x4{0, 0, 0, 0};
+        s1[nt] = f32x4{0, 0, 0, 0};
+      }
+      const int r0 = 32 * kp + krow0;
+      const int sw = kswz<D>(r0);  // same for r0 + 4
 #pragma unroll
-        for (int i = 0; i < KS; ++i) {
-          const u32x4 a0 =
-              *reinterpret_cast<const u32x4*>(&skb[(32 * kp + krow0) * KROW + 32 * i + 8 * c]);
-          const u32x4 a1 = *reinterpret_cast<const u32x4*>(
-              &skb[(32 * kp + krow0 + 4) * KROW + 32 * i + 8 * c]);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            s0[nt] = mfma16x16x32(a0, qf[nt][i], s0[nt]);
-            s1[nt] = mfma16x16x32(a1, qf[nt][i], s1[nt]);
-          }
-        }
-        // Lane group c holds keys key0 + 0..7 (0..3 from s0, 4..7 from s1).
-        const int key0 = tile * BK + 32 * kp + 8 * c;
-        u32x4 pb[NT], pl[NT];
+      for (int i = 0; i < KS; ++i) {
+        const int jj = (4 * i + c) ^ sw;
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(sb + r0 * (2 * D) + 16 * jj);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(sb + (r0 + 4) * (2 * D) + 16 * jj);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          float sc[8];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            sc[t] = (key0 + t <= lim[nt]) ? s0[nt][t] * scale_log2 : -INFINITY;
-            sc[t + 4] = (key0 + 4 + t <= lim[nt]) ? s1[nt][t] * scale_log2 : -INFINITY;
-          }
-          float mx = sc[0];
-#pragma unroll
-          for (int t = 1; t < 8; ++t) mx = fmaxf(mx, sc[t]);
-          mx = wave_xor_max(mx, 16);
-          mx = wave_xor_max(mx, 32);
-          const float m_new = fmaxf(m_run[nt], mx);
-          const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-          const float alpha = fast_exp2(m_run[nt] - m_use);
-          float psum = 0.f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float a = fast_exp2(sc[2 * e] - m_use);
-            const float b = fast_exp2(sc[2 * e + 1] - m_use);
-            const uint32_t w = pack_bf16x2(a, b);
-            pb[nt][e] = w;
-            if (HILO) {
-              pl[nt][e] = pack_bf16x2(a - bf16_bits_to_f32(w & 0xFFFFu),
-                                      b - bf16_bits_to_f32(w >> 16));
-              psum += a + b;
-            } else {
-              psum += bf16_bits_to_f32(w & 0xFFFFu) + bf16_bits_to_f32(w >> 16);
-            }
-          }
-          l_run[nt] = l_run[nt] * alpha + psum;
-          m_run[nt] = m_new;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) acc[nt][dt] *= alpha;
-        }
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const u32x4 a =
-              *reinterpret_cast<const u32x4*>(&svb[(16 * dt + col) * VROW + 32 * kp + 8 * c]);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            acc[nt][dt] = mfma16x16x32(a, pb[nt], acc[nt][dt]);
-            if (HILO) acc[nt][dt] = mfma16x16x32(a, pl[nt], acc[nt][dt]);
-          }
+          s0[nt] = mfma16x16x32(a0, qf[nt][i], s0[nt]);
+          s1[nt] = mfma16x16x32(a1, qf[nt][i], s1[nt]);
         }
       }
-    };
+      // Lane group c holds keys key0 + 0..7 (0..3 from s0, 4..7 from s1).
+      const int key0 = tile * BK + 32 * kp + 8 * c;
+      u32x4 pb[NT], pl[NT];
+      // Pairs wholly at or below every column's causal limit need no mask.
+      const bool masked = tile * BK + 32 * kp + 31 > wave_min_lim;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float sr[8];  // raw scores <q, k>
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          sr[t] = s0[nt][t];
+          sr[t + 4] = s1[nt][t];
+        }
+        bool vis[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) vis[t] = !masked || key0 + t <= lim[nt];
+        // The scale is >= 0, so the max can be taken on raw scores.
+        float mraw = vis[0] ? sr[0] : -INFINITY;
+#pragma unroll
+        for (int t = 1; t < 8; ++t) mraw = fmaxf(mraw, vis[t] ? sr[t] : -INFINITY);
+        const float mx = (mraw == -INFINITY) ? -INFINITY : mraw * scale_log2;
+        // Lazy rescaling: exponentials are taken against a reference max
+        // m_run that only moves when a score exceeds it by more than 2^8
+        // (so P <= 256, harmless in fp32/bf16).  The test is per lane but
+        // the update is wave-uniform, and when it happens the new max is
+        // reduced over the column's four lane groups, so m_run stays equal
+        // across them.
+        if (__any(mx > m_run[nt] + kRescaleLog2)) {
+          float mall = wave_xor_max(mx, 16);
+          mall = wave_xor_max(mall, 32);
+          const float m_new = fmaxf(m_run[nt], mall);
+          const float alpha = fast_exp2(m_run[nt] - ((m_new == -INFINITY) ? 0.f : m_new));
+          l_acc[nt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) acc[nt][dt] *= alpha;
+          m_run[nt] = m_new;
+        }
+        const float neg_m = (m_run[nt] == -INFINITY) ? 0.f : -m_run[nt];
+        float pv[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          pv[t] = fast_exp2(fmaf(sr[t], scale_log2, neg_m));
+          if (masked) pv[t] = vis[t] ? pv[t] : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t w = pack_bf16x2(pv[2 * e], pv[2 * e + 1]);
+          pb[nt][e] = w;
+          if (HILO)
+            pl[nt][e] = pack_bf16x2(pv[2 * e] - bf16_bits_to_f32(w & 0xFFFFu),
+                                    pv[2 * e + 1] - bf16_bits_to_f32(w >> 16));
+        }
+        l_acc[nt] = mfma16x16x32(ones, pb[nt], l_acc[nt]);
+        if (HILO) l_acc[nt] = mfma16x16x32(ones, pl[nt], l_acc[nt]);
+      }
+      // Keys at or past kend were copied from stand-in blocks or are tails:
+      // their P is 0 but 0*NaN is NaN, so zero their V values.
+      const bool vmask = tile * BK + 32 * kp + 32 > kend;
+      u32x4 keep = {~0u, ~0u, ~0u, ~0u};
+      if (vmask) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          keep[e] = ((key0 + 2 * e < kend) ? 0x0000FFFFu : 0u) |
+                    ((key0 + 2 * e + 1 < kend) ? 0xFFFF0000u : 0u);
+      }
+      const int vblk = 2 * kp + (c >> 1);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = 16 * dt + col;
+        u32x4 a = *reinterpret_cast<const u32x4*>(vb + vblk * (D * 32) + d * 32 +
+                                                   16 * ((c & 1) ^ ((d >> 3) & 1)));
+        if (vmask) a &= keep;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          acc[nt][dt] = mfma16x16x32(a, pb[nt], acc[nt][dt]);
+          if (HILO) acc[nt][dt] = mfma16x16x32(a, pl[nt], acc[nt][dt]);
+        }
+      }
+    }
+  };
+
+  // ---- pipeline: S-1 tiles issued ahead, one barrier per tile ---------------
+  // At the top of tile t, this wave has issued tiles up to min(t+S-2,
+  // ntiles-1); waiting for all but the later ones' copies leaves tile t
+  // complete for this wave, and the barrier makes it complete for all waves
+  // and guarantees everyone finished tile t-1, whose buffer the copy of tile
+  // t+S-1 then reuses.  The loop is unrolled by S so that every buffer index
+  // is a compile-time constant: the compiler can then tell the buffer being
+  // read from the buffers still being filled and inserts no wait of its own.
+  // Table entries are fetched one tile ahead of their use.
+  if (0 < ntiles) issue(entry_of(0), stage(std::integral_constant<int, 0>{}));
+  if constexpr (S >= 3)
+    if (1 < ntiles) issue(entry_of(1), stage(std::integral_constant<int, 1>{}));
+  if constexpr (S >= 4)
+    if (2 < ntiles) issue(entry_of(2), stage(std::integral_constant<int, 2>{}));
+  int64_t next_phys = entry_of(S - 1);
+  auto step = [&](int t, auto stage_tag) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stage_tag)::value;
+    const int ahead = min(S - 2, ntiles - 1 - t);  // tiles issued after t
+    if constexpr (S >= 4) {
+      if (ahead >= 2) wait_vm<2 * (KPW + VPW)>();
+      else if (ahead == 1) wait_vm<KPW + VPW>();
+      else wait_vm<0>();
+    } else if constexpr (S == 3) {
+      if (ahead >= 1) wait_vm<KPW + VPW>();
+      else wait_vm<0>();
+    } else {
+      wait_vm<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    if (t + S - 1 < ntiles) {
+      issue(next_phys, stage(std::integral_constant<int, (ST + S - 1) % S>{}));
+      next_phys = entry_of(t + S);
+    }
     // The first tile holds every key of the shortest causal rows, whose
     // outputs are averages of a few values: there P enters the matrix core
     // as a bf16 hi/lo pair so its rounding stays below the output rounding.
-    if (tile == 0)
-      run_tile(std::true_type{});
+    const uint8_t* sb = stage(std::integral_constant<int, ST>{});
+    if (t == 0)
+      run_tile(t, sb, std::true_type{});
     else
-      run_tile(std::false_type{});
-    if (tile + 1 < ntiles) stash(buf ^ 1);
-    __syncthreads();
+      run_tile(t, sb, std::false_type{});
+  };
+  for (int t0 = 0; t0 < ntiles; t0 += S) {
+    step(t0, std::integral_constant<int, 0>{});
+    if (t0 + 1 < ntiles) step(t0 + 1, std::integral_constant<int, 1>{});
+    if constexpr (S >= 3)
+      if (t0 + 2 < ntiles) step(t0 + 2, std::integral_constant<int, 2>{});
+    if constexpr (S >= 4)
+      if (t0 + 3 < ntiles) step(t0 + 3, std::integral_constant<int, 3>{});
   }
 
   const bool any_bad = __syncthreads_or(bad || bad_entry);
   const float nanv = __builtin_nanf("");
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    float l = wave_xor_sum(l_run[nt], 16);
-    l = wave_xor_sum(l, 32);
+    const float l = l_acc[nt][0];
     if (lim[nt] < 0) continue;
     const float inv = l > 0.f ? 1.f / l : 0.f;
     uint16_t* dst = out + ((int64_t)qrow[nt] * num_q_heads + qhead[nt]) * D + 4 * c;
@@ -294,19 +412,19 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(
   }
 }
 
-template <int D, int NT, int BK, int NW>
+template <int D, int NT, int BK, int NW, int S, int WPE>
 int launch_cfg(void* out, const void* q, const void* k_cache, const void* v_cache,
                const int32_t* block_tables, const int32_t* cu_seqlens,
                const int32_t* prefix_lens, int num_seqs, int total_q, int max_q_len,
                int num_q_heads, int num_kv_heads, int64_t num_blocks, int max_blocks_per_seq,
                float scale, hipStream_t stream) {
-  using Cfg = PrefillCfg<D, NT, BK, NW>;
+  using Cfg = PrefillCfg<D, NT, BK, NW, S>;
   const int group = num_q_heads / num_kv_heads;
   const int64_t cols = (int64_t)max_q_len * group;
   const int64_t nslots = (cols + Cfg::kCols - 1) / Cfg::kCols;
   const int64_t nwg = nslots * num_seqs * num_kv_heads;
   if (nwg > 0x7FFFFFFF) return -2;
-  hipLaunchKernelGGL((prefill_kernel<D, NT, BK, NW>), dim3((unsigned)nwg), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((prefill_kernel<D, NT, BK, NW, S, WPE>), dim3((unsigned)nwg), dim3(NW * 64), 0,
                      stream, (uint16_t*)out, (const uint16_t*)q, (const uint16_t*)k_cache,
                      (const uint16_t*)v_cache, block_tables, cu_seqlens, prefix_lens, num_seqs,
                      total_q, max_q_len, num_q_heads, num_kv_heads, group, num_blocks,
@@ -321,24 +439,16 @@ int launch_prefill(void* out, const void* q, const void* k_cache, const void* v_
                    const int32_t* prefix_lens, int num_seqs, int total_q, int max_q_len,
                    int num_q_heads, int num_kv_heads, int head_dim, int64_t num_blocks,
                    int max_blocks_per_seq, float scale, hipStream_t stream) {
+#define PA_PREFILL_ARGS                                                                     \
+  out, q, k_cache, v_cache, block_tables, cu_seqlens, prefix_lens, num_seqs, total_q,       \
+      max_q_len, num_q_heads, num_kv_heads, num_blocks, max_blocks_per_seq, scale, stream
   switch (head_dim) {
-    case 64:
-      return launch_cfg<64, 4, 64, 4>(out, q, k_cache, v_cache, block_tables, cu_seqlens,
-                                      prefix_lens, num_seqs, total_q, max_q_len, num_q_heads,
-                                      num_kv_heads, num_blocks, max_blocks_per_seq, scale, stream);
-    case 128:
-      return launch_cfg<128, 2, 64, 4>(out, q, k_cache, v_cache, block_tables, cu_seqlens,
-                                       prefix_lens, num_seqs, total_q, max_q_len, num_q_heads,
-                                       num_kv_heads, num_blocks, max_blocks_per_seq, scale,
-                                       stream);
-    case 256:
-      return launch_cfg<256, 2, 32, 4>(out, q, k_cache, v_cache, block_tables, cu_seqlens,
-                                       prefix_lens, num_seqs, total_q, max_q_len, num_q_heads,
-                                       num_kv_heads, num_blocks, max_blocks_per_seq, scale,
-                                       stream);
-    default:
-      return -2;
+    case 64: return launch_cfg<64, 1, 64, 8, 2, 4>(PA_PREFILL_ARGS);
+    case 128: return launch_cfg<128, 1, 32, 8, 2, 4>(PA_PREFILL_ARGS);
+    case 256: return launch_cfg<256, 1, 32, 8, 2, 1>(PA_PREFILL_ARGS);
+    default: return -2;
   }
+#undef PA_PREFILL_ARGS
 }
 
 }  // namespace pa

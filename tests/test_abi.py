@@ -104,6 +104,7 @@ def test_decode_validation(lib):
     assert _decode(lib, P=0) == INVALID
     assert _decode(lib, scale=float("nan")) == INVALID
     assert _decode(lib, scale=float("inf")) == INVALID
+    assert _decode(lib, scale=-0.5) == INVALID
     assert _decode(lib, q=None) == INVALID
     assert _decode(lib, bt=None) == INVALID
     assert _decode(lib, ctx=None) == INVALID
@@ -151,6 +152,7 @@ def test_prefill_validation(lib):
     assert _prefill(lib, bs=64) == UNSUPPORTED
     assert _prefill(lib, mb=0) == INVALID
     assert _prefill(lib, scale=float("nan")) == INVALID
+    assert _prefill(lib, scale=-1.0) == INVALID
     assert _prefill(lib, cu=None) == INVALID
     assert _prefill(lib, out=None) == INVALID
     assert _prefill(lib, S=0) == OK
