@@ -7,11 +7,15 @@ from .paged_attention import (  # noqa: F401
     BLOCK,
     bf16_bits_to_f64,
     bf16_ulp,
+    causal_visible,
     combine_partials,
     decode,
     decode_partials,
     f64_to_bf16_f64,
     gather_sequence,
+    kv_head_of,
     prefill,
+    scores,
+    softmax_rows,
     write_kv,
 )

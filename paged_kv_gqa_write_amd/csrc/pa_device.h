@@ -32,9 +32,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
-// Two fp32 -> packed bf16x2 (low half = a).
+// Two fp32 -> packed bf16x2 (low half = a), round to nearest even: one
+// v_cvt_pk_bf16_f32 through the two-lane vector conversion.
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+  const f32x2v v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
@@ -59,5 +63,17 @@ __device__ __forceinline__ float wave_xor_sum(float v, int mask) {
 
 // Uniform (scalar) copy of a wave-uniform value.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Scalar copy of a wave-uniform pointer.  Besides placing it in SGPRs, the
+// opaque readfirstlane keeps the compiler from re-associating per-lane
+// offsets into it, so `uniform_ptr(p) + lane_offset` addresses memory as
+// scalar base + 32-bit vector offset.
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
 
 }  // namespace pa

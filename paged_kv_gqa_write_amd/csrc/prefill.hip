@@ -45,7 +45,10 @@ namespace pa {
 namespace {
 
 constexpr float kLog2e = 1.44269504088896341f;
-// Reference-max slack (log2 units) before the accumulators are rescaled.
+// Softmax reference modes (see finish_pair in the kernel).
+enum { kFirst = 0, kFixed = 1, kLazy = 2 };
+// Lazy mode: reference-max slack (log2 units) before the accumulators are
+// rescaled.
 constexpr float kRescaleLog2 = 8.f;
 
 typedef const int32_t __attribute__((address_space(4)))* const_i32_ptr;
@@ -164,11 +167,14 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
   // only vector-memory operations are the tile copies counted below.
   wait_vm<0>();
 
-  int wave_min_lim = lim[0];
+  // Smallest causal limit over the wave's columns that are written (columns
+  // past the sequence take whatever the plain form gives; never stored).
+  int wave_min_lim = 0x7FFFFFFF;
 #pragma unroll
-  for (int nt = 1; nt < NT; ++nt) wave_min_lim = min(wave_min_lim, lim[nt]);
+  for (int nt = 0; nt < NT; ++nt) wave_min_lim = min(wave_min_lim, lim[nt] < 0 ? 0x7FFFFFFF : lim[nt]);
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) wave_min_lim = min(wave_min_lim, __shfl_xor(wave_min_lim, m, 64));
+  wave_min_lim = __builtin_amdgcn_readfirstlane(wave_min_lim);
 
   f32x4 acc[NT][DT];
 #pragma unroll
@@ -213,6 +219,8 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
   };
   auto issue = [&](int64_t phys, uint8_t* sb) __attribute__((always_inline)) {
     const int64_t tile_base = (phys * num_kv_heads + g) * (int64_t)(kBlock * D);
+    const uint16_t* kt = uniform_ptr(k_cache + tile_base);
+    const uint16_t* vt = uniform_ptr(v_cache + tile_base);
 #pragma unroll
     for (int k = 0; k < KPW; ++k) {
       const int m = wave * KPW + k;
@@ -220,7 +228,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
       const int off = 16 * lane;
       const int r = r0 + off / (2 * D);
       const int j = ((off % (2 * D)) / 16) ^ kswz<D>(r);
-      __builtin_amdgcn_global_load_lds(k_cache + tile_base + (r & 15) * D + 8 * j, sb + 1024 * m,
+      __builtin_amdgcn_global_load_lds(kt + (uint32_t)((r & 15) * D + 8 * j), sb + 1024 * m,
                                        16, 0, 0);
     }
 #pragma unroll
@@ -228,17 +236,134 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
       const int mv = wave * VPW + k;
       const int d = 32 * (mv % kVPerBlock) + (lane >> 1);
       const int h = (lane & 1) ^ ((d >> 3) & 1);
-      __builtin_amdgcn_global_load_lds(v_cache + tile_base + d * kBlock + 8 * h,
+      __builtin_amdgcn_global_load_lds(vt + (uint32_t)(d * kBlock + 8 * h),
                                        sb + KB + 1024 * mv, 16, 0, 0);
     }
   };
 
-  // K row of score tile t, pair kp, for this lane: key 8*(col/4) + col%4 + 4t.
+  // Per-lane byte offsets of the LDS operand reads inside a stage, fixed for
+  // the whole kernel: every read below is a lane base plus an immediate.
+  // K: score tile t of pair kp reads row r = 32*kp + krow0 + 4t, whose
+  // swizzle kswz(r) does not depend on kp or t (they only touch bits 2 and
+  // 5 up); chunk 4i+c of that row.
+  // V^T: block 2*kp + c/2 of the pair, row d = 16*dt + col, half c%1 swizzled
+  // by bit 3 of d (= bit 3 of col).
   const int krow0 = 8 * (col >> 2) + (col & 3);
+  int koff[KS];
+#pragma unroll
+  for (int i = 0; i < KS; ++i) koff[i] = krow0 * (2 * D) + 16 * ((4 * i + c) ^ kswz<D>(krow0));
+  const int voff = KB + (c >> 1) * (D * 32) + col * 32 + 16 * ((c & 1) ^ ((col >> 3) & 1));
 
-  auto run_tile = [&](int tile, const uint8_t* sb, auto hilo_tag) __attribute__((always_inline)) {
+  // Softmax and P.V of one 32-key pair whose raw scores are s0/s1.
+  //
+  // Reference max.  Exponentials are taken against a per-column reference
+  // m_run (log2 domain), in one of three modes:
+  //   kFirst  tile 0: m_run := max of the column's visible scores in the tile
+  //           (every written column sees key 0, so this is a real score).
+  //   kFixed  later tiles: m_run stays fixed.  A later score above it gives
+  //           P = 2^(z - m_run) > 1, which fp32 and bf16 represent with the
+  //           same relative precision; the pass is exact as long as nothing
+  //           overflows, which the kernel checks afterwards (row sums below
+  //           2^64, outputs finite).  No max is taken, no rescaling happens.
+  //   kLazy   the exact fallback when that check fails: m_run moves to the
+  //           new max whenever a score exceeds it by more than 2^8, and the
+  //           accumulators are rescaled then.
+  // MASK selects the form for pairs that cross a causal limit of this wave's
+  // columns or reach past the workgroup's last key; every other pair takes
+  // the plain form, which carries no per-key compares or selects.
+  auto finish_pair = [&](const uint8_t* sb, int kp, int key0, f32x4 (&s0)[NT], f32x4 (&s1)[NT],
+                         auto mode_tag, auto mask_tag, auto hilo_tag) __attribute__((always_inline)) {
+    constexpr int MODE = decltype(mode_tag)::value;
+    constexpr bool MASK = decltype(mask_tag)::value;
     constexpr bool HILO = decltype(hilo_tag)::value;
-    const uint8_t* vb = sb + KB;
+    // Keep the V^T operand reads below the score products: hoisted above
+    // them they would be live together with the K operands (> 128 VGPRs).
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 pb[NT], pl[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float sr[8];  // raw scores <q, k>
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        sr[t] = s0[nt][t];
+        sr[t + 4] = s1[nt][t];
+      }
+      bool vis[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) vis[t] = !MASK || key0 + t <= lim[nt];
+      if constexpr (MODE != kFixed) {
+        // The scale is >= 0, so the max can be taken on raw scores.
+        float mraw = vis[0] ? sr[0] : -INFINITY;
+#pragma unroll
+        for (int t = 1; t < 8; ++t) mraw = fmaxf(mraw, vis[t] ? sr[t] : -INFINITY);
+        const float mx = (mraw == -INFINITY) ? -INFINITY : mraw * scale_log2;
+        if constexpr (MODE == kFirst) {
+          // Max over the column's four lane groups; a column that sees no key
+          // (past the sequence, never written) takes 0.
+          float mall = wave_xor_max(mx, 16);
+          mall = wave_xor_max(mall, 32);
+          m_run[nt] = (mall == -INFINITY) ? 0.f : mall;
+        } else {
+          // The test is per lane but the update is wave-uniform; the new max
+          // is reduced over the column's four lane groups, so m_run stays
+          // equal across them.
+          if (__any(mx > m_run[nt] + kRescaleLog2)) {
+            float mall = wave_xor_max(mx, 16);
+            mall = wave_xor_max(mall, 32);
+            const float m_new = fmaxf(m_run[nt], mall);
+            const float alpha = fast_exp2(m_run[nt] - m_new);
+            l_acc[nt] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[nt][dt] *= alpha;
+            m_run[nt] = m_new;
+          }
+        }
+      }
+      const float neg_m = -m_run[nt];
+      float pv[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        pv[t] = fast_exp2(fmaf(sr[t], scale_log2, neg_m));
+        if (MASK) pv[t] = vis[t] ? pv[t] : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w = pack_bf16x2(pv[2 * e], pv[2 * e + 1]);
+        pb[nt][e] = w;
+        if (HILO)
+          pl[nt][e] = pack_bf16x2(pv[2 * e] - bf16_bits_to_f32(w & 0xFFFFu),
+                                  pv[2 * e + 1] - bf16_bits_to_f32(w >> 16));
+      }
+      l_acc[nt] = mfma16x16x32(ones, pb[nt], l_acc[nt]);
+      if (HILO) l_acc[nt] = mfma16x16x32(ones, pl[nt], l_acc[nt]);
+    }
+    // Keys at or past kend were copied from stand-in blocks or are tails:
+    // their P is 0 but 0*NaN is NaN, so their V values are zeroed.
+    u32x4 keep;
+    if (MASK) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        keep[e] = ((key0 + 2 * e < kend) ? 0x0000FFFFu : 0u) |
+                  ((key0 + 2 * e + 1 < kend) ? 0xFFFF0000u : 0u);
+    }
+    const uint8_t* vr = sb + voff + kp * (2 * D * 32);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      u32x4 a = *reinterpret_cast<const u32x4*>(vr + dt * (16 * 32));
+      if (MASK) a &= keep;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        acc[nt][dt] = mfma16x16x32(a, pb[nt], acc[nt][dt]);
+        if (HILO) acc[nt][dt] = mfma16x16x32(a, pl[nt], acc[nt][dt]);
+      }
+    }
+  };
+
+  // FIRST: this is tile 0, whose first pair sets the reference max; the
+  // tile's other pairs and all later tiles run in the pass's mode.
+  auto run_tile = [&](int tile, const uint8_t* sb, auto first_tag, auto mode_tag, auto hilo_tag)
+      __attribute__((always_inline)) {
+    constexpr bool FIRST = decltype(first_tag)::value;
 #pragma unroll
     for (int kp = 0; kp < BK / 32; ++kp) {
       f32x4 s0[NT], s1[NT];
@@ -247,13 +372,11 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
         s0[nt] = f32x4{0, 0, 0, 0};
         s1[nt] = f32x4{0, 0, 0, 0};
       }
-      const int r0 = 32 * kp + krow0;
-      const int sw = kswz<D>(r0);  // same for r0 + 4
 #pragma unroll
       for (int i = 0; i < KS; ++i) {
-        const int jj = (4 * i + c) ^ sw;
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(sb + r0 * (2 * D) + 16 * jj);
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(sb + (r0 + 4) * (2 * D) + 16 * jj);
+        const uint8_t* kr = sb + koff[i] + 32 * kp * (2 * D);
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(kr);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(kr + 4 * (2 * D));
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           s0[nt] = mfma16x16x32(a0, qf[nt][i], s0[nt]);
@@ -261,82 +384,17 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
         }
       }
       // Lane group c holds keys key0 + 0..7 (0..3 from s0, 4..7 from s1).
-      const int key0 = tile * BK + 32 * kp + 8 * c;
-      u32x4 pb[NT], pl[NT];
-      // Pairs wholly at or below every column's causal limit need no mask.
-      const bool masked = tile * BK + 32 * kp + 31 > wave_min_lim;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        float sr[8];  // raw scores <q, k>
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          sr[t] = s0[nt][t];
-          sr[t + 4] = s1[nt][t];
-        }
-        bool vis[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) vis[t] = !masked || key0 + t <= lim[nt];
-        // The scale is >= 0, so the max can be taken on raw scores.
-        float mraw = vis[0] ? sr[0] : -INFINITY;
-#pragma unroll
-        for (int t = 1; t < 8; ++t) mraw = fmaxf(mraw, vis[t] ? sr[t] : -INFINITY);
-        const float mx = (mraw == -INFINITY) ? -INFINITY : mraw * scale_log2;
-        // Lazy rescaling: exponentials are taken against a reference max
-        // m_run that only moves when a score exceeds it by more than 2^8
-        // (so P <= 256, harmless in fp32/bf16).  The test is per lane but
-        // the update is wave-uniform, and when it happens the new max is
-        // reduced over the column's four lane groups, so m_run stays equal
-        // across them.
-        if (__any(mx > m_run[nt] + kRescaleLog2)) {
-          float mall = wave_xor_max(mx, 16);
-          mall = wave_xor_max(mall, 32);
-          const float m_new = fmaxf(m_run[nt], mall);
-          const float alpha = fast_exp2(m_run[nt] - ((m_new == -INFINITY) ? 0.f : m_new));
-          l_acc[nt] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) acc[nt][dt] *= alpha;
-          m_run[nt] = m_new;
-        }
-        const float neg_m = (m_run[nt] == -INFINITY) ? 0.f : -m_run[nt];
-        float pv[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          pv[t] = fast_exp2(fmaf(sr[t], scale_log2, neg_m));
-          if (masked) pv[t] = vis[t] ? pv[t] : 0.f;
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t w = pack_bf16x2(pv[2 * e], pv[2 * e + 1]);
-          pb[nt][e] = w;
-          if (HILO)
-            pl[nt][e] = pack_bf16x2(pv[2 * e] - bf16_bits_to_f32(w & 0xFFFFu),
-                                    pv[2 * e + 1] - bf16_bits_to_f32(w >> 16));
-        }
-        l_acc[nt] = mfma16x16x32(ones, pb[nt], l_acc[nt]);
-        if (HILO) l_acc[nt] = mfma16x16x32(ones, pl[nt], l_acc[nt]);
-      }
-      // Keys at or past kend were copied from stand-in blocks or are tails:
-      // their P is 0 but 0*NaN is NaN, so zero their V values.
-      const bool vmask = tile * BK + 32 * kp + 32 > kend;
-      u32x4 keep = {~0u, ~0u, ~0u, ~0u};
-      if (vmask) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          keep[e] = ((key0 + 2 * e < kend) ? 0x0000FFFFu : 0u) |
-                    ((key0 + 2 * e + 1 < kend) ? 0xFFFF0000u : 0u);
-      }
-      const int vblk = 2 * kp + (c >> 1);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int d = 16 * dt + col;
-        u32x4 a = *reinterpret_cast<const u32x4*>(vb + vblk * (D * 32) + d * 32 +
-                                                   16 * ((c & 1) ^ ((d >> 3) & 1)));
-        if (vmask) a &= keep;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          acc[nt][dt] = mfma16x16x32(a, pb[nt], acc[nt][dt]);
-          if (HILO) acc[nt][dt] = mfma16x16x32(a, pl[nt], acc[nt][dt]);
-        }
+      const int pair0 = tile * BK + 32 * kp;
+      const int key0 = pair0 + 8 * c;
+      // Wave-uniform: does the pair cross a causal limit of one of this
+      // wave's columns, or reach past the keys this workgroup needs?
+      if (FIRST && kp == 0) {
+        finish_pair(sb, kp, key0, s0, s1, std::integral_constant<int, kFirst>{}, std::true_type{},
+                    hilo_tag);
+      } else if (pair0 + 31 > wave_min_lim || pair0 + 32 > kend) {
+        finish_pair(sb, kp, key0, s0, s1, mode_tag, std::true_type{}, hilo_tag);
+      } else {
+        finish_pair(sb, kp, key0, s0, s1, mode_tag, std::false_type{}, hilo_tag);
       }
     }
   };
@@ -349,50 +407,79 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
   // t+S-1 then reuses.  The loop is unrolled by S so that every buffer index
   // is a compile-time constant: the compiler can then tell the buffer being
   // read from the buffers still being filled and inserts no wait of its own.
-  // Table entries are fetched one tile ahead of their use.
-  if (0 < ntiles) issue(entry_of(0), stage(std::integral_constant<int, 0>{}));
-  if constexpr (S >= 3)
-    if (1 < ntiles) issue(entry_of(1), stage(std::integral_constant<int, 1>{}));
-  if constexpr (S >= 4)
-    if (2 < ntiles) issue(entry_of(2), stage(std::integral_constant<int, 2>{}));
-  int64_t next_phys = entry_of(S - 1);
-  auto step = [&](int t, auto stage_tag) __attribute__((always_inline)) {
-    constexpr int ST = decltype(stage_tag)::value;
-    const int ahead = min(S - 2, ntiles - 1 - t);  // tiles issued after t
-    if constexpr (S >= 4) {
-      if (ahead >= 2) wait_vm<2 * (KPW + VPW)>();
-      else if (ahead == 1) wait_vm<KPW + VPW>();
-      else wait_vm<0>();
-    } else if constexpr (S == 3) {
-      if (ahead >= 1) wait_vm<KPW + VPW>();
-      else wait_vm<0>();
-    } else {
-      wait_vm<0>();
-    }
-    __builtin_amdgcn_s_barrier();
-    if (t + S - 1 < ntiles) {
-      issue(next_phys, stage(std::integral_constant<int, (ST + S - 1) % S>{}));
-      next_phys = entry_of(t + S);
-    }
+  // Table entries are fetched one tile ahead of their use.  One pass over all
+  // tiles in the given softmax mode; on return no copy is in flight.
+  auto run_pass = [&](auto mode_tag) __attribute__((always_inline)) {
+    if (0 < ntiles) issue(entry_of(0), stage(std::integral_constant<int, 0>{}));
+    if constexpr (S >= 3)
+      if (1 < ntiles) issue(entry_of(1), stage(std::integral_constant<int, 1>{}));
+    if constexpr (S >= 4)
+      if (2 < ntiles) issue(entry_of(2), stage(std::integral_constant<int, 2>{}));
+    int64_t next_phys = entry_of(S - 1);
+    auto step = [&](int t, auto stage_tag, auto first_tag, auto hilo_tag)
+        __attribute__((always_inline)) {
+      constexpr int ST = decltype(stage_tag)::value;
+      const int ahead = min(S - 2, ntiles - 1 - t);  // tiles issued after t
+      if constexpr (S >= 4) {
+        if (ahead >= 2) wait_vm<2 * (KPW + VPW)>();
+        else if (ahead == 1) wait_vm<KPW + VPW>();
+        else wait_vm<0>();
+      } else if constexpr (S == 3) {
+        if (ahead >= 1) wait_vm<KPW + VPW>();
+        else wait_vm<0>();
+      } else {
+        wait_vm<0>();
+      }
+      __builtin_amdgcn_s_barrier();
+      if (t + S - 1 < ntiles) {
+        issue(next_phys, stage(std::integral_constant<int, (ST + S - 1) % S>{}));
+        next_phys = entry_of(t + S);
+      }
+      run_tile(t, stage(std::integral_constant<int, ST>{}), first_tag, mode_tag, hilo_tag);
+    };
     // The first tile holds every key of the shortest causal rows, whose
     // outputs are averages of a few values: there P enters the matrix core
     // as a bf16 hi/lo pair so its rounding stays below the output rounding.
-    const uint8_t* sb = stage(std::integral_constant<int, ST>{});
-    if (t == 0)
-      run_tile(t, sb, std::true_type{});
-    else
-      run_tile(t, sb, std::false_type{});
+    // It also sets the reference max.  It is peeled off the loop so that the
+    // loop body carries only the plain forms.
+    using no = std::false_type;
+    if (0 < ntiles) step(0, std::integral_constant<int, 0>{}, std::true_type{}, std::true_type{});
+    for (int t0 = 1; t0 < ntiles; t0 += S) {
+      step(t0, std::integral_constant<int, 1 % S>{}, no{}, no{});
+      if (t0 + 1 < ntiles) step(t0 + 1, std::integral_constant<int, 2 % S>{}, no{}, no{});
+      if constexpr (S >= 3)
+        if (t0 + 2 < ntiles) step(t0 + 2, std::integral_constant<int, 3 % S>{}, no{}, no{});
+      if constexpr (S >= 4)
+        if (t0 + 3 < ntiles) step(t0 + 3, std::integral_constant<int, 4 % S>{}, no{}, no{});
+    }
   };
-  for (int t0 = 0; t0 < ntiles; t0 += S) {
-    step(t0, std::integral_constant<int, 0>{});
-    if (t0 + 1 < ntiles) step(t0 + 1, std::integral_constant<int, 1>{});
-    if constexpr (S >= 3)
-      if (t0 + 2 < ntiles) step(t0 + 2, std::integral_constant<int, 2>{});
-    if constexpr (S >= 4)
-      if (t0 + 3 < ntiles) step(t0 + 3, std::integral_constant<int, 3>{});
-  }
+
+  run_pass(std::integral_constant<int, kFixed>{});
 
   const bool any_bad = __syncthreads_or(bad || bad_entry);
+  // The fixed-reference pass is exact unless a score rose more than 2^64
+  // above its column's first-tile max (or something overflowed): then the
+  // workgroup runs again with the lazily rescaled reference.
+  bool redo = false;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    if (lim[nt] < 0) continue;
+    redo |= !(l_acc[nt][0] < 0x1p64f);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) redo |= !(fabsf(acc[nt][dt][e]) < INFINITY);
+  }
+  if (__syncthreads_or(redo && !any_bad)) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      l_acc[nt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[nt][dt] = f32x4{0, 0, 0, 0};
+    }
+    run_pass(std::integral_constant<int, kLazy>{});
+  }
+
   const float nanv = __builtin_nanf("");
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {

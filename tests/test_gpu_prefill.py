@@ -107,3 +107,60 @@ def test_prefill_repeat_runs_bitwise_identical():
                                        num_q_heads=32, num_kv_heads=8, head_dim=128,
                                        num_blocks=64, seed=10)
     assert torch.equal(prefill_gpu(case), prefill_gpu(case))
+
+
+def _weight_rounding_bound(case):
+    """Per-element error bound of attention whose softmax weights enter the
+    P.V product as bf16 (fp32 accumulation, normalised by the sum of the same
+    rounded weights): with w the exact weights and |delta_j| <= 2^-9 the
+    weights' relative rounding, out' - out = sum_j w_j delta_j (v_j - out) /
+    (1 + sum_j w_j delta_j), so |out' - out| <= 2^-9 S / (1 - 2^-9) with
+    S = sum_j w_j |v_j - out|.  Returned: 2^-8 S (twice that, covering the
+    fp32 score/exp errors, orders of magnitude smaller) plus one bf16 ulp of
+    out for the output rounding.  Computed in fp64 from the oracle's own
+    helpers, with the exact output."""
+    kc, vc = prefill_oracle_pools(case)
+    qf = oracle.bf16_bits_to_f64(bits(case.q))
+    out = np.zeros(qf.shape)
+    spread = np.zeros(qf.shape)
+    bt, cu = case.block_tables.numpy(), case.cu_seqlens.numpy()
+    for s, (n, p) in enumerate(zip(case.q_lens, case.prefix_lens_list)):
+        a = int(cu[s])
+        K, V = oracle.gather_sequence(kc, vc, bt[s], p + n)
+        vis = oracle.causal_visible(p, n)
+        mask = np.arange(p + n)[None, :] < vis[:, None]
+        for h in range(case.num_q_heads):
+            g = oracle.kv_head_of(h, case.num_q_heads, case.num_kv_heads)
+            z = np.where(mask, oracle.scores(qf[a:a + n, h], K[:, g], case.scale), -np.inf)
+            w = oracle.softmax_rows(z)
+            o = w @ V[:, g]
+            out[a:a + n, h] = o
+            spread[a:a + n, h] = np.einsum("rj,rjd->rd", w,
+                                           np.abs(V[None, :, g, :] - o[:, None, :]))
+    return out, 2.0 ** -8 * spread + oracle.bf16_ulp(out)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("factor", [4.0, 64.0])
+def test_prefill_scores_rising_far_above_the_first_tile(d, factor):
+    """Keys past position 47 are scaled by `factor` (a power of two, exact in
+    bf16), so later scores climb far above every column's first-tile max:
+    by about 2^20 at factor 4 -- weights above 1 in the fixed-reference pass
+    -- and beyond the fp32 range at factor 64, where the kernel must fall
+    back to its lazily rescaled pass.  The softmax gets so peaked that the
+    bf16 rounding of the exact outputs alone exceeds the literal 4e-3, and
+    the error of bf16 weights is no longer below it either: each element is
+    held to the bound derived from the weights' rounding."""
+    announce(f"prefill rising scores d={d} factor={factor}")
+    case = workloads.make_prefill_case("rise", q_lens=[300, 200], prefix_lens=[0, 0],
+                                       num_q_heads=8, num_kv_heads=2, head_dim=d,
+                                       num_blocks=64, seed=31 + d)
+    rows = torch.cat([torch.arange(48, 300), 300 + torch.arange(48, 200)])
+    case.k_new[rows] = (case.k_new[rows].float() * factor).to(torch.bfloat16)
+    out = prefill_gpu(case).float().double().numpy()
+    ref, bound = _weight_rounding_bound(case)
+    err = np.abs(out - ref)
+    print(f"[bound] rising x{factor} d={d}: max err {err.max():.3g}, "
+          f"max err/bound {(err / bound).max():.3g}", flush=True)
+    assert np.isfinite(out).all()
+    assert (err <= bound).all(), (err - bound).max()
