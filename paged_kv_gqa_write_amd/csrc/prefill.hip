@@ -50,7 +50,7 @@ namespace pa {
 namespace {
 
 constexpr float kLog2e = 1.44269504088896341f;
-// Softmax reference modes (see finish_pair in the kernel).
+// Softmax reference modes (see softmax_pair in the kernel).
 enum { kFirst = 0, kFixed = 1, kLazy = 2 };
 // Lazy mode: reference-max slack (log2 units) before the accumulators are
 // rescaled.
@@ -93,6 +93,11 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Wait until this wave's LDS operations are complete.
+__device__ __forceinline__ void wait_lds() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
 
 template <int D, int NT, int BK, int NW, int S, int WPE>
@@ -244,6 +249,24 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
     }
   };
 
+  // Zero, in this wave's V^T copies of `tile`, the values of keys at or past
+  // kend (tails of the last live block and stand-in blocks).  Lane l of copy
+  // mv holds row d = 32*(mv % (D/32)) + l/2, keys 8*(l%2)..+7 of block
+  // mv / (D/32) of the tile.
+  auto zero_v_tail = [&](int tile, uint8_t* sb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < VPW; ++k) {
+      const int mv = wave * VPW + k;
+      const int key = tile * BK + kBlock * (mv / kVPerBlock) + 8 * (lane & 1);
+      u32x4* p = reinterpret_cast<u32x4*>(sb + KB + 1024 * mv + 16 * lane);
+      u32x4 v = *p;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        v[e] &= ((key + 2 * e < kend) ? 0x0000FFFFu : 0u) | ((key + 2 * e + 1 < kend) ? 0xFFFF0000u : 0u);
+      *p = v;
+    }
+  };
+
   // Per-lane byte offsets of the LDS operand reads inside a stage, fixed for
   // the whole kernel: every read below is a lane base plus an immediate.
   // K: score tile t of pair kp reads row r = 32*kp + krow0 + 4t, whose
@@ -259,7 +282,8 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
   for (int i = 0; i < KS; ++i) koff[i] = krow0 * (2 * D) + 16 * ((4 * i + c) ^ kswz<D>(krow0));
   const int voff = KB + (c >> 1) * (D * 32) + col * 32 + 16 * (c & 1);
 
-  // Softmax and P.V of one 32-key pair whose raw scores are s0/s1.
+  // Softmax of one 32-key pair whose raw scores are s0/s1: the bf16 weights
+  // P (and their rounding residue for HILO) as the B operand of P.V.
   //
   // Reference max.  Exponentials are taken against a per-column reference
   // m_run (log2 domain), in one of three modes:
@@ -276,15 +300,12 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
   // MASK selects the form for pairs that cross a causal limit of this wave's
   // columns or reach past the workgroup's last key; every other pair takes
   // the plain form, which carries no per-key compares or selects.
-  auto finish_pair = [&](const uint8_t* sb, int kp, int key0, f32x4 (&s0)[NT], f32x4 (&s1)[NT],
-                         auto mode_tag, auto mask_tag, auto hilo_tag) __attribute__((always_inline)) {
+  auto softmax_pair = [&](int key0, f32x4 (&s0)[NT], f32x4 (&s1)[NT], u32x4 (&pb)[NT],
+                          u32x4 (&pl)[NT], auto mode_tag, auto mask_tag, auto hilo_tag)
+      __attribute__((always_inline)) {
     constexpr int MODE = decltype(mode_tag)::value;
     constexpr bool MASK = decltype(mask_tag)::value;
     constexpr bool HILO = decltype(hilo_tag)::value;
-    // Keep the V^T operand reads below the score products: hoisted above
-    // them they would be live together with the K operands (> 128 VGPRs).
-    __builtin_amdgcn_sched_barrier(0);
-    u32x4 pb[NT], pl[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       float sr[8];  // raw scores <q, k>
@@ -339,23 +360,28 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
           pl[nt][e] = pack_bf16x2(pv[2 * e] - bf16_bits_to_f32(w & 0xFFFFu),
                                   pv[2 * e + 1] - bf16_bits_to_f32(w >> 16));
       }
+    }
+  };
+
+  // Row sums and O^T += V^T . P^T for one pair.  One form for every pair:
+  // the V^T values of keys at or past kend are zeroed in LDS beforehand
+  // (their P is 0, but 0*NaN would be NaN), so no mask is needed here and
+  // each accumulator has a single use (the matrix core updates it in place).
+  auto pv_pair = [&](const uint8_t* sb, int kp, const u32x4 (&pb)[NT], const u32x4 (&pl)[NT],
+                     auto hilo_tag) __attribute__((always_inline)) {
+    constexpr bool HILO = decltype(hilo_tag)::value;
+    // Keep the V^T operand reads below the score products: hoisted above
+    // them they would be live together with the K operands (> 128 VGPRs).
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
       l_acc[nt] = mfma16x16x32(ones, pb[nt], l_acc[nt]);
       if (HILO) l_acc[nt] = mfma16x16x32(ones, pl[nt], l_acc[nt]);
-    }
-    // Keys at or past kend were copied from stand-in blocks or are tails:
-    // their P is 0 but 0*NaN is NaN, so their V values are zeroed.
-    u32x4 keep;
-    if (MASK) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        keep[e] = ((key0 + 2 * e < kend) ? 0x0000FFFFu : 0u) |
-                  ((key0 + 2 * e + 1 < kend) ? 0xFFFF0000u : 0u);
     }
     const uint8_t* vr = sb + voff + kp * (2 * D * 32);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      u32x4 a = *reinterpret_cast<const u32x4*>(vr + dt * (16 * 32));
-      if (MASK) a &= keep;
+      const u32x4 a = *reinterpret_cast<const u32x4*>(vr + dt * (16 * 32));
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         acc[nt][dt] = mfma16x16x32(a, pb[nt], acc[nt][dt]);
@@ -366,8 +392,11 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
 
   // FIRST: this is tile 0, whose first pair sets the reference max; the
   // tile's other pairs and all later tiles run in the pass's mode.
-  auto run_tile = [&](int tile, const uint8_t* sb, auto first_tag, auto mode_tag, auto hilo_tag)
-      __attribute__((always_inline)) {
+  // after_qk runs once per tile, right after the first pair's score products
+  // are issued (the next tile's copies start there, off the path from the
+  // barrier to the first LDS reads).
+  auto run_tile = [&](int tile, const uint8_t* sb, auto first_tag, auto mode_tag, auto hilo_tag,
+                      auto&& after_qk) __attribute__((always_inline)) {
     constexpr bool FIRST = decltype(first_tag)::value;
 #pragma unroll
     for (int kp = 0; kp < BK / 32; ++kp) {
@@ -388,19 +417,23 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
           s1[nt] = mfma16x16x32(a1, qf[nt][i], s1[nt]);
         }
       }
+      if (kp == 0) after_qk();
       // Lane group c holds keys key0 + 0..7 (0..3 from s0, 4..7 from s1).
       const int pair0 = tile * BK + 32 * kp;
       const int key0 = pair0 + 8 * c;
       // Wave-uniform: does the pair cross a causal limit of one of this
       // wave's columns, or reach past the keys this workgroup needs?
+      u32x4 pb[NT], pl[NT];
+      __builtin_amdgcn_sched_barrier(0);
       if (FIRST && kp == 0) {
-        finish_pair(sb, kp, key0, s0, s1, std::integral_constant<int, kFirst>{}, std::true_type{},
-                    hilo_tag);
+        softmax_pair(key0, s0, s1, pb, pl, std::integral_constant<int, kFirst>{}, std::true_type{},
+                     hilo_tag);
       } else if (pair0 + 31 > wave_min_lim || pair0 + 32 > kend) {
-        finish_pair(sb, kp, key0, s0, s1, mode_tag, std::true_type{}, hilo_tag);
+        softmax_pair(key0, s0, s1, pb, pl, mode_tag, std::true_type{}, hilo_tag);
       } else {
-        finish_pair(sb, kp, key0, s0, s1, mode_tag, std::false_type{}, hilo_tag);
+        softmax_pair(key0, s0, s1, pb, pl, mode_tag, std::false_type{}, hilo_tag);
       }
+      pv_pair(sb, kp, pb, pl, hilo_tag);
     }
   };
 
@@ -435,12 +468,20 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
       } else {
         wait_vm<0>();
       }
-      __builtin_amdgcn_s_barrier();
-      if (t + S - 1 < ntiles) {
-        issue(next_phys, stage(std::integral_constant<int, (ST + S - 1) % S>{}));
-        next_phys = entry_of(t + S);
+      // Last tile: zero the V^T values of keys at or past kend in this wave's
+      // own copies (complete after the wait above) before publishing them.
+      if (t == ntiles - 1 && t * BK + BK > kend) {
+        zero_v_tail(t, stage(std::integral_constant<int, ST>{}));
+        wait_lds();
       }
-      run_tile(t, stage(std::integral_constant<int, ST>{}), first_tag, mode_tag, hilo_tag);
+      __builtin_amdgcn_s_barrier();
+      run_tile(t, stage(std::integral_constant<int, ST>{}), first_tag, mode_tag, hilo_tag,
+               [&]() __attribute__((always_inline)) {
+                 if (t + S - 1 < ntiles) {
+                   issue(next_phys, stage(std::integral_constant<int, (ST + S - 1) % S>{}));
+                   next_phys = entry_of(t + S);
+                 }
+               });
     };
     // The first tile holds every key of the shortest causal rows, whose
     // outputs are averages of a few values: there P enters the matrix core

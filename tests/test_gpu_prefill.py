@@ -164,3 +164,20 @@ def test_prefill_scores_rising_far_above_the_first_tile(d, factor):
           f"max err/bound {(err / bound).max():.3g}", flush=True)
     assert np.isfinite(out).all()
     assert (err <= bound).all(), (err - bound).max()
+
+
+def test_prefill_many_sequences_mixed_costs():
+    """70 sequences (more than one wave's worth, so the work-order search
+    walks the sequences in several chunks) with mixed lengths and cached
+    prefixes, hence work items of very different costs, plus an empty one:
+    every output row against the oracle."""
+    announce("prefill 70 sequences")
+    g = torch.Generator().manual_seed(70)
+    q_lens = torch.randint(1, 41, (70,), generator=g).tolist()
+    prefix_lens = torch.randint(0, 60, (70,), generator=g).tolist()
+    q_lens[33] = 0
+    case = workloads.make_prefill_case("many", q_lens=q_lens, prefix_lens=prefix_lens,
+                                       num_q_heads=8, num_kv_heads=2, head_dim=64,
+                                       num_blocks=512, seed=71)
+    out = prefill_gpu(case)
+    check_tolerance("70 sequences", out, prefill_oracle(case))
