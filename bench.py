@@ -109,7 +109,7 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
 
-    def decode_layer(i):
+    def decode_layer(i, sptr=sptr):
         st = lib.pa_write_kv(k_new.data_ptr(), v_new.data_ptr(), slots.data_ptr(),
                              kc[i].data_ptr(), vc[i].data_ptr(), B, hkv, d, 16, nb, sptr)
         st |= lib.pa_decode(out.data_ptr(), part_out.data_ptr(), part_lse.data_ptr(),
@@ -121,9 +121,9 @@ def main():
                                        ctx.data_ptr(), B, hq, d, ps, npart, sptr)
         return st
 
-    def decode_step():
+    def decode_step(sptr=sptr):
         for i in range(L):
-            if decode_layer(i) != 0:
+            if decode_layer(i, sptr) != 0:
                 raise RuntimeError("decode step launch failed")
 
     for _ in range(args.warmup):
@@ -139,6 +139,29 @@ def main():
     ms_step = t0.elapsed_time(t1) / args.steps
     kv_bytes_layer = case.kv_bytes()
     value = kv_bytes_layer * L / (ms_step * 1e-3) / 1e9
+
+    # The same step captured once as a HIP graph and replayed (the pages' decode
+    # runs as graph replay): launch overhead leaves the host, the GPU work is
+    # identical.  Reported beside the eager figure.
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        decode_step(side.cuda_stream)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        decode_step(torch.cuda.current_stream(dev).cuda_stream)
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        graph.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    graph_ms_step = t0.elapsed_time(t1) / args.steps
+    del graph
 
     # Decode kernel alone: the same K steps' pa_decode launches issued back to
     # back on the launch stream between one pair of HIP events (pa_write_kv
@@ -192,6 +215,10 @@ def main():
                    "head_dim": d, "block_size": 16, "context_lens": case.context_lens.tolist(),
                    "num_blocks_per_layer": nb, "partition_size": ps, "num_partitions": npart},
         "roofline": roofline,
+        "decode_step_graph": {"ms_per_step": round(graph_ms_step, 4),
+                              "value": round(kv_bytes_layer * L / (graph_ms_step * 1e-3) / 1e9, 1),
+                              "unit": "GB/s",
+                              "note": "same step captured once as a HIP graph and replayed"},
     }
 
     # ---------------- prefill: Qwen3-4B shape, 4 x 1024 ----------------------
