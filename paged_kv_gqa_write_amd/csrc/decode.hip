@@ -314,26 +314,37 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
 // One wave per (sequence, query head).  Lane p holds partition p's LSE (64
 // partitions per chunk), so the max and the weights take one load; weights
 // are broadcast with readlane and each lane accumulates its D/64 elements.
+// The context length, the first chunk of LSEs and the first PF partitions'
+// pieces are all loaded up front from in-bounds addresses (masked once the
+// length is known), so the kernel waits for memory once, not three times.
 template <int D>
 __global__ __launch_bounds__(64) void decode_reduce_kernel(
     uint16_t* __restrict__ out, const float* __restrict__ part_out,
     const float* __restrict__ part_lse, const int32_t* __restrict__ context_lens,
     int num_q_heads, int partition_size, int num_partitions) {
   constexpr int EPT = D / 64;
+  constexpr int PF = 16;
   const int64_t row = blockIdx.x;  // s * Hq + h
   const int s = (int)(row / num_q_heads);
   const int lane = threadIdx.x;
+  const float* lse = part_lse + row * num_partitions;
+  const float* po = part_out + row * num_partitions * D + lane * EPT;
+  const int ctx = context_lens != nullptr ? context_lens[s] : 0;
+  const float lse0 = lse[min(lane, num_partitions - 1)];
+  float pre[PF][EPT];
+#pragma unroll
+  for (int p = 0; p < PF; ++p)
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) pre[p][e] = po[(int64_t)min(p, num_partitions - 1) * D + e];
+
   int np = num_partitions;
-  if (context_lens != nullptr) {
-    const int ctx = context_lens[s];
+  if (context_lens != nullptr)
     np = ctx <= 0 ? 0 : (int)min((int64_t)num_partitions,
                                  ((int64_t)ctx + partition_size - 1) / partition_size);
-  }
-  const float* lse = part_lse + row * num_partitions;
   float M = -INFINITY;
   bool nan_seen = false;
   for (int p0 = 0; p0 < np; p0 += 64) {
-    const float v = (p0 + lane < np) ? lse[p0 + lane] : -INFINITY;
+    const float v = (p0 + lane < np) ? (p0 == 0 ? lse0 : lse[p0 + lane]) : -INFINITY;
     nan_seen |= v != v;
     M = fmaxf(M, v);
   }
@@ -346,12 +357,26 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(
   for (int e = 0; e < EPT; ++e) o[e] = 0.f;
   float L = 0.f;
   if (M != -INFINITY) {
-    const float* po = part_out + row * num_partitions * D + lane * EPT;
     for (int p0 = 0; p0 < np; p0 += 64) {
-      const float w = (p0 + lane < np) ? fast_exp2((lse[p0 + lane] - M) * kLog2e) : 0.f;
+      const float lv = p0 == 0 ? lse0 : lse[min(p0 + lane, num_partitions - 1)];
+      const float w = (p0 + lane < np) ? fast_exp2((lv - M) * kLog2e) : 0.f;
       const int cnt = min(64, np - p0);
+      int j = 0;
+      if (p0 == 0) {
+        // Pieces already in registers.
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+          if (p < cnt) {
+            const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), p));
+            L += wj;
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) o[e] += wj * pre[p][e];
+          }
+        }
+        j = min(PF, cnt);
+      }
 #pragma unroll 4
-      for (int j = 0; j < cnt; ++j) {
+      for (; j < cnt; ++j) {
         const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
         L += wj;
         const float* src = po + (int64_t)(p0 + j) * D;
