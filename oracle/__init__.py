@@ -10,6 +10,8 @@ from .paged_attention import (  # noqa: F401
     causal_visible,
     combine_partials,
     decode,
+    decode_multi,
+    decode_multi_partials,
     decode_partials,
     f64_to_bf16_f64,
     gather_sequence,

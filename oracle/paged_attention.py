@@ -18,6 +18,12 @@ What is computed (the pages print no formula; this is the plainest reading):
     cache on by default): a prefill whose prompt starts with cached blocks
     computes only the new tokens, which attend to the cached prefix and,
     causally, to each other.
+  * Same page, section DSpark Speculative Decoding: the target model checks
+    a block of drafted tokens in one pass.  Read here as decode with T query
+    tokens per sequence, all already appended to the cache: token t of T
+    sits at position ctx - T + t and sees keys 0..ctx - T + t (causal within
+    the block, full over the cached context), exactly as those tokens would
+    be computed as a prefill whose cached prefix is the first ctx - T tokens.
   * Attention itself is scaled dot-product softmax attention:
       z_j = scale * <q, k_j>,   w_j = exp(z_j) / sum_i exp(z_i),
       out = sum_j w_j v_j,
@@ -235,14 +241,15 @@ def decode_partials(q, k_cache, v_cache, block_tables, context_lens, scale,
 def combine_partials(part_out, part_lse) -> np.ndarray:
     """Log-sum-exp combination of split-K pieces:
         out = sum_p exp(lse_p) O_p / sum_p exp(lse_p)
-    (max-shifted); all partitions empty gives 0."""
+    (max-shifted); all partitions empty gives 0.  part_out [..., P, D],
+    part_lse [..., P] (any leading dimensions: [B, Hq] or [B, T, Hq])."""
     lse = np.asarray(part_lse, dtype=np.float64)
     po = np.asarray(part_out, dtype=np.float64)
     M = np.max(lse, axis=-1, keepdims=True)
     M = np.where(np.isfinite(M), M, 0.0)
-    w = np.exp(lse - M)                                    # [B, Hq, P]
+    w = np.exp(lse - M)                                    # [..., P]
     den = np.sum(w, axis=-1)
-    num = np.einsum("bhp,bhpd->bhd", w, po)
+    num = np.einsum("...p,...pd->...d", w, po)
     return np.divide(num, den[..., None], out=np.zeros_like(num), where=den[..., None] > 0)
 
 
@@ -266,3 +273,66 @@ def prefill(q, k_cache, v_cache, block_tables, cu_seqlens, prefix_lens, scale,
         visible = causal_visible(P, N)
         out[a:b] = attend(qf[a:b], K, V, scale, visible, num_q_heads, num_kv_heads)
     return out
+
+
+def decode_multi(q, k_cache, v_cache, block_tables, context_lens, scale,
+                 num_q_heads, num_kv_heads) -> np.ndarray:
+    """Decode with T query tokens per sequence (verifying a drafted block).
+
+    q: bf16 bits [B, T, Hq, D].  context_lens[s] counts all cached tokens of
+    sequence s, its T query tokens included.  Token t sits at position
+    ctx - T + t and sees keys 0..ctx - T + t.  ctx == 0 gives zeros;
+    0 < ctx < T (query tokens at negative positions) gives NaN.
+    Returns fp64 [B, T, Hq, D]."""
+    qf = bf16_bits_to_f64(q)
+    B, T = qf.shape[0], qf.shape[1]
+    out = np.zeros(qf.shape, dtype=np.float64)
+    for s in range(B):
+        n = int(context_lens[s])
+        if n == 0:
+            continue
+        if n < T:
+            out[s] = np.nan
+            continue
+        K, V = gather_sequence(k_cache, v_cache, block_tables[s], n)
+        visible = causal_visible(n - T, T)
+        out[s] = attend(qf[s], K, V, scale, visible, num_q_heads, num_kv_heads)
+    return out
+
+
+def decode_multi_partials(q, k_cache, v_cache, block_tables, context_lens, scale,
+                          num_q_heads, num_kv_heads, partition_size, num_partitions):
+    """Split-K pieces of decode_multi.  For token t of sequence s the visible
+    keys are [0, ctx - T + t + 1); partition p covers [p*ps, (p+1)*ps) of
+    them.  For each (s, t, h, p):
+        part_out = sum_{j in p, visible} exp(z_j) v_j / sum exp(z_j)
+        part_lse = log sum_{j in p, visible} exp(z_j)
+    and 0 / -inf where partition p holds no visible key."""
+    qf = bf16_bits_to_f64(q)
+    B, T, Hq, D = qf.shape
+    P = num_partitions
+    part_out = np.zeros((B, T, Hq, P, D), dtype=np.float64)
+    part_lse = np.full((B, T, Hq, P), -np.inf, dtype=np.float64)
+    for s in range(B):
+        n = int(context_lens[s])
+        if n == 0:
+            continue
+        if n < T:
+            part_out[s] = np.nan
+            part_lse[s] = np.nan
+            continue
+        K, V = gather_sequence(k_cache, v_cache, block_tables[s], n)
+        vis = causal_visible(n - T, T)
+        for t in range(T):
+            for p in range(P):
+                lo, hi = p * partition_size, min(int(vis[t]), (p + 1) * partition_size)
+                if lo >= hi:
+                    continue
+                for h in range(Hq):
+                    g = kv_head_of(h, Hq, num_kv_heads)
+                    z = scores(qf[s, t, h, :][None, :], K[lo:hi, g, :], scale)[0]
+                    m = np.max(z)
+                    e = np.exp(z - m)
+                    part_out[s, t, h, p] = (e @ V[lo:hi, g, :]) / np.sum(e)
+                    part_lse[s, t, h, p] = m + np.log(np.sum(e))
+    return part_out, part_lse

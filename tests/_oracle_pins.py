@@ -389,6 +389,98 @@ def pin_partials_combine_equals_unsplit():
         assert np.allclose(oracle.combine_partials(po, pl), full, rtol=1e-12, atol=1e-14), ps
 
 
+# ---------------------------------------------------------------------------
+# Several query tokens per sequence (verifying a drafted block)
+# ---------------------------------------------------------------------------
+
+def pin_brute_decode_multi():
+    """Token t of T at position ctx-T+t sees keys 0..ctx-T+t: 50-digit brute
+    force per (sequence, token, head); ctx == 0 gives zeros, 0 < ctx < T NaN."""
+    gen = torch.Generator().manual_seed(4321)
+    for (hq, hkv, d), T in zip(SHAPES, [3, 8, 1, 2, 5]):
+        lens = [T, 16, 17 + T, 40]
+        bt, kc, vc, K, V = _tiny_paged(gen, lens, hq, hkv, d)
+        q = random_bf16_bits(gen, (len(lens), T, hq, d))
+        qf = oracle.bf16_bits_to_f64(q)
+        scale = 1.3 / math.sqrt(d)
+        out = oracle.decode_multi(q, kc, vc, bt, lens, scale, hq, hkv)
+        assert out.shape == (len(lens), T, hq, d)
+        G = hq // hkv
+        for s, L in enumerate(lens):
+            for t in range(T):
+                n_vis = L - T + t + 1
+                for h in range(hq):
+                    g = h // G
+                    want, _ = _brute_attention(qf[s, t, h], K[s][:n_vis, g], V[s][:n_vis, g], scale)
+                    assert np.allclose(out[s, t, h], want, rtol=1e-12, atol=1e-13), (hq, s, t, h)
+    bt, kc, vc, K, V = _tiny_paged(gen, [5, 5], 2, 1, 4)
+    q = random_bf16_bits(gen, (2, 4, 2, 4))
+    out = oracle.decode_multi(q, kc, vc, bt, [0, 3], 0.5, 2, 1)
+    assert np.array_equal(out[0], np.zeros((4, 2, 4))), out[0]
+    assert np.isnan(out[1]).all()
+
+
+def pin_closed_forms_decode_multi():
+    """Identical keys: token t's output is the mean of V over its window
+    0..ctx-T+t exactly; one visible key gives that key's V."""
+    gen = torch.Generator().manual_seed(77)
+    hq, hkv, d, T = 4, 2, 8, 6
+    lens = [6, 29]
+    bt, kc, vc, K, V = _tiny_paged(gen, lens, hq, hkv, d)
+    row = kc[bt[0][0], :, 0, :].copy()
+    for s, L in enumerate(lens):
+        for p in range(L):
+            kc[bt[s][p // 16], :, p % 16, :] = row
+    q = random_bf16_bits(gen, (2, T, hq, d))
+    out = oracle.decode_multi(q, kc, vc, bt, lens, 0.8, hq, hkv)
+    for s, L in enumerate(lens):
+        for t in range(T):
+            n_vis = L - T + t + 1
+            for h in range(hq):
+                want = V[s][:n_vis, h // 2].mean(axis=0)
+                assert np.allclose(out[s, t, h], want, rtol=1e-13, atol=1e-14), (s, t, h)
+    # ctx == T: token 0 sees only itself
+    for h in range(hq):
+        assert np.array_equal(out[0, 0, h], V[0][0, h // 2])
+
+
+def pin_decode_multi_invariants():
+    """T = 1 is decode; every T equals a prefill of the T tokens after a
+    cached prefix of ctx - T; the split-K pieces combine to the unsplit result
+    and match 50-digit brute force piece by piece."""
+    from workloads import make_decode_case
+    c = make_decode_case("m", context_lens=[9, 33, 70], num_q_heads=8, num_kv_heads=2,
+                         head_dim=8, num_blocks=16, seed=13, poison=False)
+    q1, kc, vc, bt, ctx = _case_bits(c)
+    got = oracle.decode_multi(q1[:, None], kc, vc, bt, ctx, c.scale, 8, 2)[:, 0]
+    assert np.array_equal(got, oracle.decode(q1, kc, vc, bt, ctx, c.scale, 8, 2))
+    gen = torch.Generator().manual_seed(14)
+    T = 7
+    q = random_bf16_bits(gen, (3, T, 8, 8))
+    multi = oracle.decode_multi(q, kc, vc, bt, ctx, c.scale, 8, 2)
+    cu = np.arange(4, dtype=np.int32) * T
+    pre = oracle.prefill(q.reshape(3 * T, 8, 8), kc, vc, bt, cu, ctx - T, c.scale, 8, 2)
+    assert np.allclose(multi.reshape(3 * T, 8, 8), pre, rtol=1e-13, atol=1e-14)
+    for ps, P in [(16, 5), (32, 3), (80, 1)]:
+        po, pl = oracle.decode_multi_partials(q, kc, vc, bt, ctx, c.scale, 8, 2, ps, P)
+        assert np.allclose(oracle.combine_partials(po, pl), multi, rtol=1e-12, atol=1e-14), ps
+    po, pl = oracle.decode_multi_partials(q, kc, vc, bt, ctx, c.scale, 8, 2, 16, 5)
+    qf = oracle.bf16_bits_to_f64(q)
+    for s, L in enumerate(ctx):
+        Ks, Vs = oracle.gather_sequence(kc, vc, bt[s], int(L))
+        for t in (0, T - 1):
+            for h in (0, 5):
+                g = h // 4
+                for p in range(5):
+                    lo, hi = p * 16, min(int(L) - T + t + 1, (p + 1) * 16)
+                    if hi <= lo:
+                        assert pl[s, t, h, p] == -math.inf and not po[s, t, h, p].any()
+                        continue
+                    want, lse = _brute_attention(qf[s, t, h], Ks[lo:hi, g], Vs[lo:hi, g], c.scale)
+                    assert np.allclose(po[s, t, h, p], want, rtol=1e-12, atol=1e-13)
+                    assert abs(pl[s, t, h, p] - lse) < 1e-12
+
+
 ALL_PINS = [
     pin_golden_cases,
     pin_bf16_conversions,
@@ -402,4 +494,7 @@ ALL_PINS = [
     pin_causal_perturbation_and_prefill_vs_decode,
     pin_gqa_equals_repeated_mha,
     pin_partials_combine_equals_unsplit,
+    pin_brute_decode_multi,
+    pin_closed_forms_decode_multi,
+    pin_decode_multi_invariants,
 ]

@@ -40,6 +40,13 @@ MUTATIONS = {
     "prefill_prefix_not_gathered": ("gather_sequence(k_cache, v_cache, block_tables[s], P + N)",
                                     "gather_sequence(k_cache, v_cache, block_tables[s], N)"),
     "bf16_round_truncates": ("np.rint(np.ldexp(m, 8))", "np.trunc(np.ldexp(m, 8))"),
+    "multi_window_shifted": ("visible = causal_visible(n - T, T)\n        out[s] = attend",
+                             "visible = causal_visible(n - T + 1, T)\n        out[s] = attend"),
+    "multi_tokens_reversed": ("out[s] = attend(qf[s], K, V, scale, visible",
+                              "out[s] = attend(qf[s][::-1], K, V, scale, visible"),
+    "multi_short_context_not_nan": ("            out[s] = np.nan\n", "            pass\n"),
+    "multi_partials_ignore_causal": ("lo, hi = p * partition_size, min(int(vis[t]), (p + 1) * partition_size)",
+                                     "lo, hi = p * partition_size, min(n, (p + 1) * partition_size)"),
 }
 
 
