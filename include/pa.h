@@ -147,6 +147,59 @@ int pa_decode_reduce(void* out, const float* part_out, const float* part_lse,
                      int32_t partition_size, int32_t num_partitions, void* stream);
 
 /*
+ * pa_decode_multi -- decode with T = query_len query tokens per sequence:
+ * the target-model pass that verifies a block of drafted tokens in
+ * speculative decoding ("Qwen3-4B / 8B / 32B", section DSpark Speculative
+ * Decoding: a drafter proposes a block of tokens and the target model checks
+ * them greedily in one forward pass).  pa_decode is the case T = 1.
+ *
+ * context_lens[s] counts every cached token of sequence s, including its T
+ * query tokens, whose K/V must already be in the pool (e.g. written by
+ * pa_write_kv on the same stream).  Query token t (0 <= t < T) sits at
+ * position ctx - T + t and attends to keys 0..ctx - T + t: the cached
+ * context plus, causally, the query tokens up to itself.  A sequence with
+ * context_lens[s] == 0 gets zero outputs; 0 < context_lens[s] < T is
+ * invalid and gives NaN outputs for that sequence.
+ *
+ * Split-K exactly as for pa_decode, one piece per (s, t, h, p):
+ *   num_partitions == 1: writes out[s, t, h, :] (bf16); part_out/part_lse
+ *     unused (may be NULL).
+ *   num_partitions  > 1: writes
+ *       part_out[s, t, h, p, :] = sum_{j in p, j visible to t} e^{z_j} v_j / sum e^{z_j}
+ *       part_lse[s, t, h, p]    = ln sum_{j in p, j visible to t} e^{z_j}
+ *     (0 and -inf where no key of p is visible to t); `out` is not touched.
+ *     pa_decode_multi_reduce then produces `out`.
+ *
+ *   out            device, bf16 [num_seqs, T, Hq, D]
+ *   part_out       device, fp32 [num_seqs, T, Hq, num_partitions, D]
+ *   part_lse       device, fp32 [num_seqs, T, Hq, num_partitions]
+ *   q              device, bf16 [num_seqs, T, Hq, D]
+ *   query_len      T, 1..16 (larger: PA_ERR_UNSUPPORTED)
+ *   other arguments as for pa_decode.
+ */
+int pa_decode_multi(void* out, float* part_out, float* part_lse,
+                    const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t query_len, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                    int64_t num_blocks, int32_t max_blocks_per_seq,
+                    int32_t partition_size, int32_t num_partitions,
+                    float scale, void* stream);
+
+/*
+ * pa_decode_multi_reduce -- pa_decode_reduce for pa_decode_multi's pieces:
+ * combines part_out[s, t, h, :, :] / part_lse[s, t, h, :] into
+ * out[s, t, h, :] (bf16 [num_seqs, T, Hq, D]) with the same formula, zero
+ * and NaN rules.  context_lens (or NULL) as for pa_decode_reduce: when given,
+ * partitions p < ceil(ctx/partition_size) of every token are read.
+ * pa_decode_reduce is the case T = 1.
+ */
+int pa_decode_multi_reduce(void* out, const float* part_out, const float* part_lse,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t query_len,
+                           int32_t num_q_heads, int32_t head_dim,
+                           int32_t partition_size, int32_t num_partitions, void* stream);
+
+/*
  * pa_prefill -- varlen causal prefill over the paged cache with cached
  * prefixes ("Qwen3-4B / 8B / 32B", sections Warm Prefix-Cache TTFT and
  * Architecture Notes: prefix cache on by default).

@@ -18,7 +18,8 @@ import torch
 
 __all__ = [
     "PAError", "load_library", "library_path", "write_kv", "decode", "decode_partials",
-    "decode_reduce", "prefill", "decode_split_plan", "status_string", "EXPORTED_SYMBOLS",
+    "decode_reduce", "decode_multi", "decode_multi_partials", "decode_multi_reduce", "prefill",
+    "decode_split_plan", "status_string", "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -37,6 +38,10 @@ _SIGNATURES = {
     "pa_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                  _i32, _i64, _i32, _i32, _i32, _f32, _vp]),
     "pa_decode_reduce": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pa_decode_multi": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                       _i32, _i32, _i32, _i64, _i32, _i32, _i32, _f32, _vp]),
+    "pa_decode_multi_reduce": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                              _i32, _vp]),
     "pa_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                   _i32, _i32, _i32, _i64, _i32, _f32, _vp]),
     "pa_decode_split_plan": (ctypes.c_int, [_i32, _i32, _i32, _i32, _pi32, _pi32]),
@@ -241,3 +246,87 @@ def prefill(q, k_cache, v_cache, block_tables, cu_seqlens, prefix_lens, scale, m
                                    block_tables.shape[1], float(scale), _stream(q.device))
     _check(st, "pa_prefill")
     return out
+
+
+# ---------------------------------------------------------------------------
+# Several query tokens per sequence (verifying a block of drafted tokens)
+# ---------------------------------------------------------------------------
+
+def _decode_multi_call(out, part_out, part_lse, q, k_cache, v_cache, block_tables, context_lens,
+                       scale, partition_size, num_partitions):
+    nb, hkv, d = _pools(k_cache, v_cache)
+    _need(q, "q", torch.bfloat16, 4)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    B, T, hq, dq = q.shape
+    if dq != d or block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("q [B, T, Hq, D], block_tables [B, max_blocks], context_lens [B] "
+                         "mismatch")
+    ptr = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
+    st = load_library().pa_decode_multi(ptr(out), ptr(part_out), ptr(part_lse), q.data_ptr(),
+                                        k_cache.data_ptr(), v_cache.data_ptr(),
+                                        block_tables.data_ptr(), context_lens.data_ptr(), B, T,
+                                        hq, hkv, d, BLOCK_SIZE, nb, block_tables.shape[1],
+                                        int(partition_size), int(num_partitions), float(scale),
+                                        _stream(q.device))
+    _check(st, "pa_decode_multi")
+
+
+def decode_multi_partials(q, k_cache, v_cache, block_tables, context_lens, scale,
+                          partition_size, num_partitions, part_out=None, part_lse=None):
+    """Split-K pieces of a multi-token decode (num_partitions > 1):
+    (part_out [B, T, Hq, P, D], part_lse [B, T, Hq, P])."""
+    B, T, hq, d = q.shape
+    if part_out is None:
+        part_out = torch.empty(B, T, hq, num_partitions, d, dtype=torch.float32, device=q.device)
+    if part_lse is None:
+        part_lse = torch.empty(B, T, hq, num_partitions, dtype=torch.float32, device=q.device)
+    _decode_multi_call(None, part_out, part_lse, q, k_cache, v_cache, block_tables,
+                       context_lens, scale, partition_size, num_partitions)
+    return part_out, part_lse
+
+
+def decode_multi_reduce(part_out, part_lse, context_lens, partition_size, out=None):
+    """Log-sum-exp combine of multi-token split-K pieces into bf16 [B, T, Hq, D]."""
+    _need(part_out, "part_out", torch.float32, 5)
+    _need(part_lse, "part_lse", torch.float32, 4)
+    B, T, hq, P, d = part_out.shape
+    if context_lens is not None:
+        _need(context_lens, "context_lens", torch.int32, 1)
+    if out is None:
+        out = torch.empty(B, T, hq, d, dtype=torch.bfloat16, device=part_out.device)
+    st = load_library().pa_decode_multi_reduce(
+        out.data_ptr(), part_out.data_ptr(), part_lse.data_ptr(),
+        0 if context_lens is None else context_lens.data_ptr(), B, T, hq, d,
+        int(partition_size), P, _stream(part_out.device))
+    _check(st, "pa_decode_multi_reduce")
+    return out
+
+
+def decode_multi(q, k_cache, v_cache, block_tables, context_lens, scale, *,
+                 max_context_len=None, partition_size=None, num_partitions=None, out=None,
+                 part_out=None, part_lse=None):
+    """Decode attention with T query tokens per sequence -> bf16 [B, T, Hq, D].
+
+    context_lens counts every cached token including the T query tokens
+    (whose K/V are already in the pool); token t sits at position
+    ctx - T + t and sees keys 0..ctx - T + t."""
+    B, T, hq, d = q.shape
+    if out is None:
+        out = torch.empty(B, T, hq, d, dtype=torch.bfloat16, device=q.device)
+    if partition_size is None or num_partitions is None:
+        if max_context_len is None:
+            max_context_len = int(context_lens.max().item()) if B > 0 else 0
+        if partition_size is None:
+            partition_size, num_partitions = decode_split_plan(B, k_cache.shape[1],
+                                                               max_context_len)
+        else:
+            num_partitions = max(1, -(-max_context_len // partition_size))
+    if num_partitions == 1:
+        _decode_multi_call(out, None, None, q, k_cache, v_cache, block_tables, context_lens,
+                           scale, partition_size, 1)
+        return out
+    part_out, part_lse = decode_multi_partials(q, k_cache, v_cache, block_tables, context_lens,
+                                               scale, partition_size, num_partitions, part_out,
+                                               part_lse)
+    return decode_multi_reduce(part_out, part_lse, context_lens, partition_size, out=out)

@@ -1,8 +1,10 @@
 // Paged GQA decode: split-K flash-decoding over block-tabled KV, plus the
-// log-sum-exp reduce of the split-K pieces.
+// log-sum-exp reduce of the split-K pieces.  The same kernel serves decode
+// with several query tokens per sequence (verifying a block of drafted
+// tokens): every (query token, query head) pair of a KV head is one column.
 //
-// Work decomposition: one workgroup per (partition p, KV head g, sequence s),
-// NW waves per workgroup.  The partition's KV blocks are taken two at a time
+// Work decomposition: one workgroup per (partition p, KV head g, sequence s,
+// column chunk), NW waves per workgroup.  The partition's KV blocks are taken two at a time
 // ("pairs", 32 keys); wave w handles a contiguous range of pairs.  All G
 // query heads of the KV head are processed together, so each K/V byte is read
 // once.  A wave fetches the block-table entries of up to 32 pairs with one
@@ -10,7 +12,9 @@
 // NBUF pairs of K/V loads in flight in a ring of register buffers.
 //
 // Both contractions run on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16),
-// with the query heads as the 16-wide N dimension (zero-padded when G < 16):
+// with the columns -- (query token, query head) pairs, G heads per token --
+// as the N dimension in NT tiles of 16 (padded when the count is not a
+// multiple of 16); every tile reuses the pair's K/V registers:
 //   S^T[key][head]  = K[key][:]   . Q^T[:][head]   (A = K rows, B = Q)
 //   O^T[d][head]   += V^T[d][key] . P^T[key][head] (A = V^T rows, B = P)
 // The score accumulator layout (lane l holds rows 4*(l/16)+r of column l%16)
@@ -36,6 +40,7 @@ namespace pa {
 namespace {
 
 constexpr float kLn2 = 0.693147180559945309f;
+constexpr int64_t kComputeUnits = 256;  // MI355X
 constexpr float kLog2e = 1.44269504088896341f;
 
 template <int D>
@@ -75,47 +80,61 @@ __device__ __forceinline__ void load_pair(PairRegs<D>& r, const uint16_t* __rest
   }
 }
 
-template <int D>
-__device__ __forceinline__ void compute_pair(PairRegs<D>& r, const u32x4 (&qf)[D / 32],
-                                             f32x4 (&acc)[D / 16], float& m_run, float& l_run,
-                                             int base_pos, int limit, float scale_log2) {
+// One pair of blocks for the NT column tiles.  Column (lane%16) of tile nt
+// sees the keys below climit[nt] (its token's causal limit, at most `limit`,
+// the end of the partition's valid keys).
+template <int D, int NT>
+__device__ __forceinline__ void compute_pair(PairRegs<D>& r, const u32x4 (&qf)[NT][D / 32],
+                                             f32x4 (&acc)[NT][D / 16], float (&m_run)[NT],
+                                             float (&l_run)[NT], int base_pos, int limit,
+                                             const int (&climit)[NT], float scale_log2) {
   // Scores: tile 0 holds keys 8*(c&1)+0..3, tile 1 keys 8*(c&1)+4..7 of the
   // lane group's block.
-  f32x4 s0 = {0, 0, 0, 0}, s1 = {0, 0, 0, 0};
+  f32x4 s0[NT], s1[NT];
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) {
-    s0 = mfma16x16x32(r.k[0][i], qf[i], s0);
-    s1 = mfma16x16x32(r.k[1][i], qf[i], s1);
+  for (int nt = 0; nt < NT; ++nt) {
+    s0[nt] = f32x4{0, 0, 0, 0};
+    s1[nt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+      s0[nt] = mfma16x16x32(r.k[0][i], qf[nt][i], s0[nt]);
+      s1[nt] = mfma16x16x32(r.k[1][i], qf[nt][i], s1[nt]);
+    }
   }
-  float sc[8];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    sc[t] = (base_pos + t < limit) ? s0[t] * scale_log2 : -INFINITY;
-    sc[t + 4] = (base_pos + 4 + t < limit) ? s1[t] * scale_log2 : -INFINITY;
-  }
-  float mx = sc[0];
-#pragma unroll
-  for (int t = 1; t < 8; ++t) mx = fmaxf(mx, sc[t]);
-  mx = wave_xor_max(mx, 16);
-  mx = wave_xor_max(mx, 32);
-  const float m_new = fmaxf(m_run, mx);
-  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-  const float alpha = fast_exp2(m_run - m_use);
   // P as a bf16 hi + lo pair: the two products together carry ~16 mantissa
   // bits of P, so rounding P costs nothing even when a few keys dominate.
-  u32x4 pb_hi, pb_lo;
-  float psum = 0.f;
+  u32x4 pb_hi[NT], pb_lo[NT];
+  float alpha[NT];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float a = fast_exp2(sc[2 * e] - m_use);
-    const float b = fast_exp2(sc[2 * e + 1] - m_use);
-    const uint32_t hi = pack_bf16x2(a, b);
-    pb_hi[e] = hi;
-    pb_lo[e] = pack_bf16x2(a - bf16_bits_to_f32(hi & 0xFFFFu), b - bf16_bits_to_f32(hi >> 16));
-    psum += a + b;
+  for (int nt = 0; nt < NT; ++nt) {
+    float sc[8];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      sc[t] = (base_pos + t < climit[nt]) ? s0[nt][t] * scale_log2 : -INFINITY;
+      sc[t + 4] = (base_pos + 4 + t < climit[nt]) ? s1[nt][t] * scale_log2 : -INFINITY;
+    }
+    float mx = sc[0];
+#pragma unroll
+    for (int t = 1; t < 8; ++t) mx = fmaxf(mx, sc[t]);
+    mx = wave_xor_max(mx, 16);
+    mx = wave_xor_max(mx, 32);
+    const float m_new = fmaxf(m_run[nt], mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    alpha[nt] = fast_exp2(m_run[nt] - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = fast_exp2(sc[2 * e] - m_use);
+      const float b = fast_exp2(sc[2 * e + 1] - m_use);
+      const uint32_t hi = pack_bf16x2(a, b);
+      pb_hi[nt][e] = hi;
+      pb_lo[nt][e] =
+          pack_bf16x2(a - bf16_bits_to_f32(hi & 0xFFFFu), b - bf16_bits_to_f32(hi >> 16));
+      psum += a + b;
+    }
+    l_run[nt] = l_run[nt] * alpha[nt] + psum;
+    m_run[nt] = m_new;
   }
-  l_run = l_run * alpha + psum;
-  m_run = m_new;
   // Keys past the valid range may hold anything (NaN included); their P is 0
   // but 0*NaN is NaN, so zero their V values before the product.
   if (base_pos + 8 > limit) {
@@ -128,27 +147,43 @@ __device__ __forceinline__ void compute_pair(PairRegs<D>& r, const u32x4 (&qf)[D
     for (int dt = 0; dt < D / 16; ++dt) r.v[dt] &= keep;
   }
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) {
-    acc[dt] *= alpha;
-    acc[dt] = mfma16x16x32(r.v[dt], pb_hi, acc[dt]);
-    acc[dt] = mfma16x16x32(r.v[dt], pb_lo, acc[dt]);
-  }
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      acc[nt][dt] *= alpha[nt];
+      acc[nt][dt] = mfma16x16x32(r.v[dt], pb_hi[nt], acc[nt][dt]);
+      acc[nt][dt] = mfma16x16x32(r.v[dt], pb_lo[nt], acc[nt][dt]);
+    }
 }
 
-template <int D, int NW, int NBUF>
+// Query tokens per sequence: query_len; columns per KV head: query_len *
+// group, taken NT tiles of 16 at a time by `num_chunks` workgroups.  The
+// chunks of one (partition, KV head, sequence) read the same K/V, so they
+// are given launch indices that are equal modulo 8: the hardware deals
+// workgroups to the 8 XCDs round-robin, so they run on one XCD and share
+// its L2.
+template <int D, int NW, int NBUF, int NT>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(
     uint16_t* __restrict__ out, float* __restrict__ part_out, float* __restrict__ part_lse,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
-    const int32_t* __restrict__ context_lens, int num_q_heads, int num_kv_heads, int group,
-    int64_t num_blocks, int max_blocks, int blocks_per_part, int num_partitions,
-    float scale_log2) {
+    const int32_t* __restrict__ context_lens, int query_len, int num_q_heads, int num_kv_heads,
+    int group, int64_t num_blocks, int max_blocks, int blocks_per_part, int num_partitions,
+    int num_chunks, float scale_log2) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
-  const int wg = blockIdx.x;
-  const int p = wg % num_partitions;
-  const int g = (wg / num_partitions) % num_kv_heads;
-  const int s = wg / (num_partitions * num_kv_heads);
+  int item = blockIdx.x, chunk = 0;
+  if (num_chunks > 1) {
+    const int items = gridDim.x / num_chunks;
+    const int base = (blockIdx.x / (8 * num_chunks)) * 8;
+    const int width = min(8, items - base);
+    const int r = blockIdx.x - base * num_chunks;
+    chunk = r / width;
+    item = base + r % width;
+  }
+  const int p = item % num_partitions;
+  const int g = (item / num_partitions) % num_kv_heads;
+  const int s = item / (num_partitions * num_kv_heads);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int col = lane & 15;
@@ -176,28 +211,45 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
   const int nblk = ctx > 0 ? (int)(((int64_t)ctx + kBlock - 1) / kBlock) : 0;
   bool bad = ctx < 0 || nblk > max_blocks ||
              (int64_t)ctx > (int64_t)num_partitions * blocks_per_part * kBlock ||
-             (nblk > 0 && num_blocks <= 0);
+             (nblk > 0 && num_blocks <= 0) || (ctx > 0 && ctx < query_len);
   const int pb1 = bad ? pb0 : min(pb0 + blocks_per_part, nblk);
   const int limit = min(ctx, pb1 * kBlock);
   const int npairs = pb1 > pb0 ? (pb1 - pb0 + 1) / 2 : 0;
   const int k1 = min((full_pairs * (wave + 1)) / NW, npairs);
   const int nk = max(k1 - k0, 0);
 
-  // Q of head col of the group.  Columns past the group read head 0 instead:
-  // each column's softmax is independent and those columns are never
-  // written, so their values do not matter.
-  u32x4 qf[KS];
-  {
-    const uint16_t* qb = q + ((int64_t)s * num_q_heads + (int64_t)g * group +
-                              (col < group ? col : 0)) * D + 8 * c;
+  // Column j = (chunk*NT + nt)*16 + col is query token j / group, head
+  // j % group of the KV head.  Token t sits at position ctx - query_len + t
+  // and sees the keys below ctx - query_len + t + 1.  Columns past the last
+  // token read token 0, head 0 instead: each column's softmax is independent
+  // and those columns are never written, so their values do not matter.
+  const int ncols = query_len * group;
+  int crow[NT];    // output row (s*query_len + t)*Hq + head, or -1
+  int climit[NT];  // keys visible to the column, within this partition
+  u32x4 qf[NT][KS];
 #pragma unroll
-    for (int i = 0; i < KS; ++i) qf[i] = load16(qb + 32 * i);
+  for (int nt = 0; nt < NT; ++nt) {
+    const int j = (chunk * NT + nt) * 16 + col;
+    const bool live = j < ncols;
+    const int t = live ? j / group : 0;
+    const int hh = live ? j - t * group : 0;
+    const int row = ((s * query_len + t) * num_q_heads) + g * group + hh;
+    crow[nt] = live ? row : -1;
+    climit[nt] = min(limit, ctx - query_len + t + 1);
+    const uint16_t* qb = q + (int64_t)row * D + 8 * c;
+#pragma unroll
+    for (int i = 0; i < KS; ++i) qf[nt][i] = load16(qb + 32 * i);
   }
 
-  f32x4 acc[DT];
+  f32x4 acc[NT][DT];
+  float m_run[NT], l_run[NT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0, 0, 0, 0};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[nt][dt] = f32x4{0, 0, 0, 0};
+    m_run[nt] = -INFINITY;
+    l_run[nt] = 0.f;
+  }
 
   // Lane group c's keys start at block (c >= 2 ? y : x), offset 8*(c&1).
   const int lane_key0 = ((c >= 2) ? kBlock : 0) + 8 * (c & 1);
@@ -230,88 +282,107 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
     for (int b = 0; b < NBUF; ++b) {
       const int k = kb + b;
       if (k < nk) {
-        compute_pair<D>(buf[b], qf, acc, m_run, l_run, (wb0 + 2 * k) * kBlock + lane_key0, limit,
-                        scale_log2);
+        compute_pair<D, NT>(buf[b], qf, acc, m_run, l_run, (wb0 + 2 * k) * kBlock + lane_key0,
+                            limit, climit, scale_log2);
         if (k + NBUF < nk) issue(k + NBUF, buf[b]);
       }
     }
   }
 
-  // Per-wave totals: l over the four lane groups of each head.
-  l_run = wave_xor_sum(l_run, 16);
-  l_run = wave_xor_sum(l_run, 32);
+  // Per-wave totals: l over the four lane groups of each column.
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    l_run[nt] = wave_xor_sum(l_run[nt], 16);
+    l_run[nt] = wave_xor_sum(l_run[nt], 32);
+  }
 
-  // Merge the NW waves: common max M per head, then waves 1..NW-1 hand their
-  // rescaled accumulators to wave 0 through LDS (fixed order: deterministic).
-  __shared__ float sm_m[NW][16];
-  __shared__ float sm_l[NW][16];
-  __shared__ f32x4 sm_o[NW > 1 ? NW - 1 : 1][DT][64];
+  // Merge the NW waves: common max M per column, then waves 1..NW-1 hand
+  // their rescaled accumulators to wave 0 through LDS (fixed order:
+  // deterministic).
+  __shared__ float sm_m[NW][NT][16];
+  __shared__ float sm_l[NW][NT][16];
+  __shared__ f32x4 sm_o[NW > 1 ? NW - 1 : 1][NT][DT][64];
   if (lane < 16) {
-    sm_m[wave][col] = m_run;
-    sm_l[wave][col] = l_run;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      sm_m[wave][nt][col] = m_run[nt];
+      sm_l[wave][nt][col] = l_run[nt];
+    }
   }
   const bool any_bad = __syncthreads_or(bad);
-  float M = -INFINITY;
+  float M[NT], L[NT];
 #pragma unroll
-  for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][col]);
-  float L = 0.f, f = 0.f;
-  if (M != -INFINITY) {
+  for (int nt = 0; nt < NT; ++nt) {
+    M[nt] = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) L += sm_l[w][col] * fast_exp2(sm_m[w][col] - M);
-    f = fast_exp2(m_run - M);
+    for (int w = 0; w < NW; ++w) M[nt] = fmaxf(M[nt], sm_m[w][nt][col]);
+    L[nt] = 0.f;
+    float f = 0.f;
+    if (M[nt] != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) L[nt] += sm_l[w][nt][col] * fast_exp2(sm_m[w][nt][col] - M[nt]);
+      f = fast_exp2(m_run[nt] - M[nt]);
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[nt][dt] *= f;
   }
   if (NW > 1) {
     if (wave > 0) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) sm_o[wave - 1][dt][lane] = acc[dt] * f;
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) sm_o[wave - 1][nt][dt][lane] = acc[nt][dt];
     }
     __syncthreads();
     if (wave > 0) return;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      f32x4 a = acc[dt] * f;
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int w = 0; w < NW - 1; ++w) a += sm_o[w][dt][lane];
-      acc[dt] = a;
-    }
-  } else {
+      for (int dt = 0; dt < DT; ++dt) {
+        f32x4 a = acc[nt][dt];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[dt] *= f;
+        for (int w = 0; w < NW - 1; ++w) a += sm_o[w][nt][dt][lane];
+        acc[nt][dt] = a;
+      }
   }
 
-  // Wave 0 writes: lane (col, c) holds head col, d = 16*dt + 4*c + r.
-  if (col >= group) return;
-  const int64_t head = (int64_t)s * num_q_heads + (int64_t)g * group + col;
-  const float inv = L > 0.f ? 1.f / L : 0.f;
+  // Wave 0 writes: lane (col, c) holds column col of each tile, d = 16*dt +
+  // 4*c + r.
   const float nanv = __builtin_nanf("");
-  if (num_partitions == 1) {
-    uint16_t* dst = out + head * D + 4 * c;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      f32x4 o = acc[dt] * inv;
-      if (any_bad) o = f32x4{nanv, nanv, nanv, nanv};
-      u32x2 w;
-      w[0] = pack_bf16x2(o[0], o[1]);
-      w[1] = pack_bf16x2(o[2], o[3]);
-      *reinterpret_cast<u32x2*>(dst + 16 * dt) = w;
-    }
-  } else {
-    float* dst = part_out + (head * num_partitions + p) * D + 4 * c;
+  for (int nt = 0; nt < NT; ++nt) {
+    if (crow[nt] < 0) continue;
+    const int64_t row = crow[nt];
+    const float inv = L[nt] > 0.f ? 1.f / L[nt] : 0.f;
+    if (num_partitions == 1) {
+      uint16_t* dst = out + row * D + 4 * c;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      f32x4 o = acc[dt] * inv;
-      if (any_bad) o = f32x4{nanv, nanv, nanv, nanv};
-      *reinterpret_cast<f32x4*>(dst + 16 * dt) = o;
-    }
-    if (c == 0) {
-      float lse = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
-      if (any_bad) lse = nanv;
-      part_lse[head * num_partitions + p] = lse;
+      for (int dt = 0; dt < DT; ++dt) {
+        f32x4 o = acc[nt][dt] * inv;
+        if (any_bad) o = f32x4{nanv, nanv, nanv, nanv};
+        u32x2 w;
+        w[0] = pack_bf16x2(o[0], o[1]);
+        w[1] = pack_bf16x2(o[2], o[3]);
+        *reinterpret_cast<u32x2*>(dst + 16 * dt) = w;
+      }
+    } else {
+      float* dst = part_out + (row * num_partitions + p) * D + 4 * c;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        f32x4 o = acc[nt][dt] * inv;
+        if (any_bad) o = f32x4{nanv, nanv, nanv, nanv};
+        *reinterpret_cast<f32x4*>(dst + 16 * dt) = o;
+      }
+      if (c == 0) {
+        float lse = L[nt] > 0.f ? (M[nt] + fast_log2(L[nt])) * kLn2 : -INFINITY;
+        if (any_bad) lse = nanv;
+        part_lse[row * num_partitions + p] = lse;
+      }
     }
   }
 }
 
-// One wave per (sequence, query head).  Lane p holds partition p's LSE (64
+// One wave per output row (sequence, query token, query head).  Lane p holds partition p's LSE (64
 // partitions per chunk), so the max and the weights take one load; weights
 // are broadcast with readlane and each lane accumulates its D/64 elements.
 // The context length, the first chunk of LSEs and the first PF partitions'
@@ -321,11 +392,11 @@ template <int D>
 __global__ __launch_bounds__(64) void decode_reduce_kernel(
     uint16_t* __restrict__ out, const float* __restrict__ part_out,
     const float* __restrict__ part_lse, const int32_t* __restrict__ context_lens,
-    int num_q_heads, int partition_size, int num_partitions) {
+    int rows_per_seq, int partition_size, int num_partitions) {
   constexpr int EPT = D / 64;
   constexpr int PF = 16;
-  const int64_t row = blockIdx.x;  // s * Hq + h
-  const int s = (int)(row / num_q_heads);
+  const int64_t row = blockIdx.x;  // (s * query_len + t) * Hq + h
+  const int s = (int)(row / rows_per_seq);
   const int lane = threadIdx.x;
   const float* lse = part_lse + row * num_partitions;
   const float* po = part_out + row * num_partitions * D + lane * EPT;
@@ -398,38 +469,53 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(
 
 int launch_decode(void* out, float* part_out, float* part_lse, const void* q,
                   const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                  const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
-                  int head_dim, int64_t num_blocks, int max_blocks_per_seq, int partition_size,
-                  int num_partitions, float scale, hipStream_t stream) {
+                  const int32_t* context_lens, int num_seqs, int query_len, int num_q_heads,
+                  int num_kv_heads, int head_dim, int64_t num_blocks, int max_blocks_per_seq,
+                  int partition_size, int num_partitions, float scale, hipStream_t stream) {
   const int group = num_q_heads / num_kv_heads;
-  const int64_t nwg = (int64_t)num_partitions * num_kv_heads * num_seqs;
+  const int tiles = (query_len * group + 15) / 16;
+  // Up to two column tiles share a wave's K/V registers; more tiles are
+  // spread over column chunks (separate workgroups on the same XCD).  Two
+  // tiles per wave halve the K/V reads per column but double a wave's math
+  // and its accumulators (one wave per SIMD); when even then the launch
+  // would not give every compute unit a workgroup, one tile per workgroup
+  // and twice the workgroups finish sooner.
+  const int64_t items = (int64_t)num_partitions * num_kv_heads * num_seqs;
+  const int nt = (tiles >= 2 && items * ((tiles + 1) / 2) >= kComputeUnits) ? 2 : 1;
+  const int chunks = (tiles + nt - 1) / nt;
+  const int64_t nwg = items * chunks;
+  if (nwg > 0x7FFFFFFF) return -2;
   const float scale_log2 = scale * kLog2e;
   const int bpp = partition_size / kBlock;
   constexpr int NW = 4;
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(NW * 64), 0, stream, (uint16_t*)out,
                        part_out, part_lse, (const uint16_t*)q, (const uint16_t*)k_cache,
-                       (const uint16_t*)v_cache, block_tables, context_lens, num_q_heads,
-                       num_kv_heads, group, num_blocks, max_blocks_per_seq, bpp,
-                       num_partitions, scale_log2);
+                       (const uint16_t*)v_cache, block_tables, context_lens, query_len,
+                       num_q_heads, num_kv_heads, group, num_blocks, max_blocks_per_seq, bpp,
+                       num_partitions, chunks, scale_log2);
   };
-  switch (head_dim) {
-    case 64: go(decode_kernel<64, NW, 4>); break;
-    case 128: go(decode_kernel<128, NW, 1>); break;
-    case 256: go(decode_kernel<256, NW, 2>); break;
+  switch (head_dim * 4 + nt) {
+    case 64 * 4 + 1: go(decode_kernel<64, NW, 4, 1>); break;
+    case 64 * 4 + 2: go(decode_kernel<64, NW, 4, 2>); break;
+    case 128 * 4 + 1: go(decode_kernel<128, NW, 1, 1>); break;
+    case 128 * 4 + 2: go(decode_kernel<128, NW, 1, 2>); break;
+    case 256 * 4 + 1: go(decode_kernel<256, NW, 2, 1>); break;
+    case 256 * 4 + 2: go(decode_kernel<256, NW, 1, 2>); break;
     default: return -2;
   }
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
 int launch_decode_reduce(void* out, const float* part_out, const float* part_lse,
-                         const int32_t* context_lens, int num_seqs, int num_q_heads,
-                         int head_dim, int partition_size, int num_partitions,
+                         const int32_t* context_lens, int num_seqs, int query_len,
+                         int num_q_heads, int head_dim, int partition_size, int num_partitions,
                          hipStream_t stream) {
-  const int64_t rows = (int64_t)num_seqs * num_q_heads;
+  const int rows_per_seq = query_len * num_q_heads;
+  const int64_t rows = (int64_t)num_seqs * rows_per_seq;
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3((unsigned)rows), dim3(64), 0, stream, (uint16_t*)out, part_out,
-                       part_lse, context_lens, num_q_heads, partition_size, num_partitions);
+                       part_lse, context_lens, rows_per_seq, partition_size, num_partitions);
   };
   switch (head_dim) {
     case 64: go(decode_reduce_kernel<64>); break;

@@ -12,6 +12,7 @@ namespace {
 
 constexpr int kBlockSize = 16;
 constexpr int kMaxGroup = 16;
+constexpr int kMaxQueryLen = 16;
 constexpr int64_t kMaxGrid = 0x7FFFFFFF;
 
 bool supported_head_dim(int32_t d) { return d == 64 || d == 128 || d == 256; }
@@ -43,42 +44,73 @@ int pa_write_kv(const void* k_new, const void* v_new, const int64_t* slot_mappin
                              num_kv_heads, head_dim, num_blocks, as_stream(stream));
 }
 
-int pa_decode(void* out, float* part_out, float* part_lse, const void* q, const void* k_cache,
-              const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
-              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-              int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
-              int32_t partition_size, int32_t num_partitions, float scale, void* stream) {
+int pa_decode_multi(void* out, float* part_out, float* part_lse, const void* q,
+                    const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t query_len,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
+                    int32_t partition_size, int32_t num_partitions, float scale, void* stream) {
   if (num_seqs < 0 || num_blocks < 0) return PA_ERR_INVALID_ARG;
+  if (query_len < 1) return PA_ERR_INVALID_ARG;
+  if (query_len > kMaxQueryLen) return PA_ERR_UNSUPPORTED;
   int st = check_heads(num_q_heads, num_kv_heads, head_dim, block_size);
   if (st != PA_OK) return st;
   if (max_blocks_per_seq <= 0) return PA_ERR_INVALID_ARG;
   if (partition_size <= 0 || partition_size % kBlockSize != 0) return PA_ERR_INVALID_ARG;
   if (num_partitions < 1) return PA_ERR_INVALID_ARG;
   if (!isfinite(scale) || scale < 0.f) return PA_ERR_INVALID_ARG;
-  if ((int64_t)num_partitions * num_kv_heads * num_seqs > kMaxGrid) return PA_ERR_UNSUPPORTED;
+  // Launch size (one workgroup per 32 columns of a partition) and the
+  // number of output rows both index with 32-bit integers.
+  const int64_t chunks = ((int64_t)query_len * (num_q_heads / num_kv_heads) + 31) / 32;
+  if ((int64_t)num_partitions * num_kv_heads * num_seqs * chunks > kMaxGrid)
+    return PA_ERR_UNSUPPORTED;
+  if ((int64_t)num_seqs * query_len * num_q_heads > kMaxGrid) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
   if (num_partitions == 1 && !out) return PA_ERR_INVALID_ARG;
   if (num_partitions > 1 && (!part_out || !part_lse)) return PA_ERR_INVALID_ARG;
   return pa::launch_decode(out, part_out, part_lse, q, k_cache, v_cache, block_tables,
-                           context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                           num_blocks, max_blocks_per_seq, partition_size, num_partitions,
-                           scale, as_stream(stream));
+                           context_lens, num_seqs, query_len, num_q_heads, num_kv_heads,
+                           head_dim, num_blocks, max_blocks_per_seq, partition_size,
+                           num_partitions, scale, as_stream(stream));
+}
+
+int pa_decode(void* out, float* part_out, float* part_lse, const void* q, const void* k_cache,
+              const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+              int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
+              int32_t partition_size, int32_t num_partitions, float scale, void* stream) {
+  return pa_decode_multi(out, part_out, part_lse, q, k_cache, v_cache, block_tables,
+                         context_lens, num_seqs, 1, num_q_heads, num_kv_heads, head_dim,
+                         block_size, num_blocks, max_blocks_per_seq, partition_size,
+                         num_partitions, scale, stream);
+}
+
+int pa_decode_multi_reduce(void* out, const float* part_out, const float* part_lse,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t query_len,
+                           int32_t num_q_heads, int32_t head_dim, int32_t partition_size,
+                           int32_t num_partitions, void* stream) {
+  if (num_seqs < 0 || num_q_heads <= 0) return PA_ERR_INVALID_ARG;
+  if (query_len < 1) return PA_ERR_INVALID_ARG;
+  if (query_len > kMaxQueryLen) return PA_ERR_UNSUPPORTED;
+  if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+  if (partition_size <= 0 || partition_size % kBlockSize != 0) return PA_ERR_INVALID_ARG;
+  if (num_partitions < 1) return PA_ERR_INVALID_ARG;
+  if ((int64_t)query_len * num_q_heads > kMaxGrid) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)num_seqs * query_len * num_q_heads > kMaxGrid) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !part_out || !part_lse) return PA_ERR_INVALID_ARG;
+  return pa::launch_decode_reduce(out, part_out, part_lse, context_lens, num_seqs, query_len,
+                                  num_q_heads, head_dim, partition_size, num_partitions,
+                                  as_stream(stream));
 }
 
 int pa_decode_reduce(void* out, const float* part_out, const float* part_lse,
                      const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                      int32_t head_dim, int32_t partition_size, int32_t num_partitions,
                      void* stream) {
-  if (num_seqs < 0 || num_q_heads <= 0) return PA_ERR_INVALID_ARG;
-  if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
-  if (partition_size <= 0 || partition_size % kBlockSize != 0) return PA_ERR_INVALID_ARG;
-  if (num_partitions < 1) return PA_ERR_INVALID_ARG;
-  if ((int64_t)num_seqs * num_q_heads > kMaxGrid) return PA_ERR_UNSUPPORTED;
-  if (num_seqs == 0) return PA_OK;
-  if (!out || !part_out || !part_lse) return PA_ERR_INVALID_ARG;
-  return pa::launch_decode_reduce(out, part_out, part_lse, context_lens, num_seqs, num_q_heads,
-                                  head_dim, partition_size, num_partitions, as_stream(stream));
+  return pa_decode_multi_reduce(out, part_out, part_lse, context_lens, num_seqs, 1, num_q_heads,
+                                head_dim, partition_size, num_partitions, stream);
 }
 
 int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -92,3 +92,28 @@ def check_tolerance(name, gpu_out, ref, literal=None):
         else:
             assert rep["mean_abs"] <= 2 * rep["floor_mean_abs"], rep
     return rep
+
+
+def decode_multi_gpu(case, partition_size=None, num_partitions=None, write_new=True):
+    kc = case.k_cache.to(DEV)
+    vc = case.v_cache.to(DEV)
+    if write_new:
+        pa.write_kv(case.k_new.to(DEV), case.v_new.to(DEV), case.slot_mapping.to(DEV), kc, vc)
+    out = pa.decode_multi(case.q.to(DEV), kc, vc, case.block_tables.to(DEV),
+                          case.context_lens.to(DEV), case.scale,
+                          max_context_len=int(case.context_lens.max()),
+                          partition_size=partition_size, num_partitions=num_partitions)
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+def decode_multi_oracle_pools(case):
+    return oracle.write_kv(bits(case.k_cache), bits(case.v_cache), bits(case.k_new),
+                           bits(case.v_new), case.slot_mapping.numpy())
+
+
+def decode_multi_oracle(case):
+    kc, vc = decode_multi_oracle_pools(case)
+    return oracle.decode_multi(bits(case.q), kc, vc, case.block_tables.numpy(),
+                               case.context_lens.numpy(), case.scale, case.num_q_heads,
+                               case.num_kv_heads)

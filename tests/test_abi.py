@@ -30,6 +30,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert header_functions() == sorted(["pa_write_kv", "pa_decode", "pa_decode_reduce",
+                                         "pa_decode_multi", "pa_decode_multi_reduce",
                                          "pa_prefill", "pa_decode_split_plan",
                                          "pa_status_string"])
 
@@ -132,6 +133,59 @@ def test_reduce_validation(lib):
     assert _reduce(lib, po=None) == INVALID
     assert _reduce(lib, pl=None) == INVALID
     assert _reduce(lib, B=0, out=None, po=None, pl=None) == OK
+
+
+def _multi(lib, **kw):
+    a = dict(out=FAKE, po=FAKE, pl=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, ctx=FAKE, B=4, T=8,
+             hq=32, hkv=8, d=128, bs=16, nb=4096, mb=72, ps=288, P=4, scale=0.088)
+    a.update(kw)
+    return lib.pa_decode_multi(a["out"], a["po"], a["pl"], a["q"], a["kc"], a["vc"], a["bt"],
+                               a["ctx"], a["B"], a["T"], a["hq"], a["hkv"], a["d"], a["bs"],
+                               a["nb"], a["mb"], a["ps"], a["P"], a["scale"], None)
+
+
+def test_decode_multi_validation(lib):
+    assert _multi(lib, T=0) == INVALID
+    assert _multi(lib, T=-3) == INVALID
+    assert _multi(lib, T=17) == UNSUPPORTED          # more than 16 query tokens
+    assert _multi(lib, B=-1) == INVALID
+    assert _multi(lib, hq=30) == INVALID
+    assert _multi(lib, hq=136, hkv=4) == UNSUPPORTED
+    assert _multi(lib, d=96) == UNSUPPORTED
+    assert _multi(lib, bs=32) == UNSUPPORTED
+    assert _multi(lib, mb=0) == INVALID
+    assert _multi(lib, ps=40) == INVALID
+    assert _multi(lib, P=0) == INVALID
+    assert _multi(lib, scale=float("nan")) == INVALID
+    assert _multi(lib, scale=-1.0) == INVALID
+    assert _multi(lib, q=None) == INVALID
+    assert _multi(lib, ctx=None) == INVALID
+    assert _multi(lib, P=1, out=None) == INVALID
+    assert _multi(lib, P=4, po=None) == INVALID
+    assert _multi(lib, P=0x10000000, B=8) == UNSUPPORTED  # grid too large
+    assert _multi(lib, B=0x1000000, T=16, hq=256, hkv=16) == UNSUPPORTED  # rows overflow int32
+    assert _multi(lib, B=0, q=None, kc=None, vc=None, bt=None, ctx=None, out=None) == OK
+
+
+def _multi_reduce(lib, **kw):
+    a = dict(out=FAKE, po=FAKE, pl=FAKE, ctx=FAKE, B=4, T=8, hq=32, d=128, ps=288, P=4)
+    a.update(kw)
+    return lib.pa_decode_multi_reduce(a["out"], a["po"], a["pl"], a["ctx"], a["B"], a["T"],
+                                      a["hq"], a["d"], a["ps"], a["P"], None)
+
+
+def test_decode_multi_reduce_validation(lib):
+    assert _multi_reduce(lib, T=0) == INVALID
+    assert _multi_reduce(lib, T=17) == UNSUPPORTED
+    assert _multi_reduce(lib, B=-1) == INVALID
+    assert _multi_reduce(lib, hq=0) == INVALID
+    assert _multi_reduce(lib, d=48) == UNSUPPORTED
+    assert _multi_reduce(lib, ps=8) == INVALID
+    assert _multi_reduce(lib, P=0) == INVALID
+    assert _multi_reduce(lib, out=None) == INVALID
+    assert _multi_reduce(lib, pl=None) == INVALID
+    assert _multi_reduce(lib, B=0x1000000, T=16, hq=256) == UNSUPPORTED
+    assert _multi_reduce(lib, B=0, out=None, po=None, pl=None) == OK
 
 
 def _prefill(lib, **kw):

@@ -103,6 +103,40 @@ class PrefillCase:
         return 4 * self.head_dim * self.num_q_heads * pairs
 
 
+@dataclass
+class MultiDecodeCase:
+    """Decode with query_len (T) query tokens per sequence: the pass that
+    verifies a block of drafted tokens."""
+    name: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    num_blocks: int
+    scale: float
+    query_len: int
+    context_lens: torch.Tensor      # int32 [B]; includes the T query tokens
+    block_tables: torch.Tensor      # int32 [B, max_blocks]; padding = -1
+    k_cache: torch.Tensor           # bf16 [NB, Hkv, 16, D]
+    v_cache: torch.Tensor           # bf16 [NB, Hkv, D, 16]
+    q: torch.Tensor                 # bf16 [B, T, Hq, D]
+    k_new: torch.Tensor             # bf16 [B*T, Hkv, D]  K of the query tokens
+    v_new: torch.Tensor             # bf16 [B*T, Hkv, D]
+    slot_mapping: torch.Tensor      # int64 [B*T]; slots of positions ctx-T..ctx-1
+    sigma: float = 1.0
+
+    @property
+    def batch(self) -> int:
+        return int(self.context_lens.numel())
+
+    @property
+    def max_blocks(self) -> int:
+        return int(self.block_tables.shape[1])
+
+    def kv_bytes(self) -> int:
+        """Algorithmic K+V bytes one pass must read (each cached token once)."""
+        return int(self.context_lens.sum()) * 2 * self.num_kv_heads * self.head_dim * 2
+
+
 def _normal_bf16(g, shape, sigma, device="cpu"):
     if device == "cpu":
         x = torch.randn(*shape, generator=g, dtype=torch.float32)
@@ -216,6 +250,42 @@ def make_prefill_case(name, *, q_lens, prefix_lens, num_q_heads, num_kv_heads, h
                        bt, kc, vc, q, k_new, v_new, slots, sigma)
 
 
+def make_multi_decode_case(name, *, query_len, context_lens=None, ctx_range=None, batch=None,
+                           num_q_heads, num_kv_heads, head_dim, num_blocks, sigma=1.0,
+                           scale=None, seed=42, max_blocks=None, poison=True, permute=True):
+    """Same draw order as make_decode_case; q is [B, T, Hq, D] and the T
+    query tokens' K/V (positions ctx-T..ctx-1) are drawn as k_new/v_new.
+    A sequence with 0 < ctx < T (invalid) gets slot -1 for positions < 0."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    T = int(query_len)
+    if context_lens is None:
+        lo, hi = ctx_range
+        ctx = torch.randint(lo, hi + 1, (batch,), generator=g, dtype=torch.int64)
+    else:
+        ctx = torch.tensor(list(context_lens), dtype=torch.int64)
+    nblk = [(int(c) + BLOCK_SIZE - 1) // BLOCK_SIZE for c in ctx]
+    if max_blocks is None:
+        max_blocks = max(nblk) if nblk else 1
+    bt = _assign_blocks(g, num_blocks, nblk, max_blocks, permute)
+    kc = _normal_bf16(g, (num_blocks, num_kv_heads, BLOCK_SIZE, head_dim), sigma)
+    vc = _normal_bf16(g, (num_blocks, num_kv_heads, head_dim, BLOCK_SIZE), sigma)
+    B = int(ctx.numel())
+    q = _normal_bf16(g, (B, T, num_q_heads, head_dim), sigma)
+    k_new = _normal_bf16(g, (B * T, num_kv_heads, head_dim), sigma)
+    v_new = _normal_bf16(g, (B * T, num_kv_heads, head_dim), sigma)
+    slots = []
+    for s in range(B):
+        n = int(ctx[s])
+        slots += [slot_of(bt, s, n - T + t) if n - T + t >= 0 else -1 for t in range(T)]
+    slots = torch.tensor(slots, dtype=torch.int64)
+    if poison:
+        poison_pool(kc, vc, bt, [max(int(c) - T, 0) for c in ctx])
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    return MultiDecodeCase(name, num_q_heads, num_kv_heads, head_dim, num_blocks, float(scale),
+                           T, ctx.to(torch.int32), bt, kc, vc, q, k_new, v_new, slots, sigma)
+
+
 # ---------------------------------------------------------------------------
 # The five workloads.  Sizes are the ones the serving pages measure on, per
 # the shapes listed in the module docstring.
@@ -269,6 +339,16 @@ def hybrid_prefill(seed=42, poison=True):
     return make_prefill_case("hybrid_prefill_4097", q_lens=[4097], prefix_lens=[0],
                              num_q_heads=16, num_kv_heads=2, head_dim=256, num_blocks=8192,
                              sigma=0.5, scale=1.0 / 16.0, seed=seed, poison=poison)
+
+
+def qwen3_4b_verify(batch=4, seed=42, poison=True):
+    """Verifying a drafted block on Qwen3-4B: the last accepted token plus 7
+    drafted ones (T = 8) per sequence, batch 4 (the pages' concurrency 4; 1
+    for single-stream), context U{1024..1152}, 32/8 heads, head_dim 128."""
+    return make_multi_decode_case(f"qwen3_4b_verify_b{batch}_t8", query_len=8,
+                                  ctx_range=(1024, 1152), batch=batch, num_q_heads=32,
+                                  num_kv_heads=8, head_dim=128, num_blocks=4096, max_blocks=72,
+                                  seed=seed, poison=poison)
 
 
 DECODE_CASES = {
