@@ -11,7 +11,9 @@ Architecture Notes): for every layer, the 8 new tokens' K/V are appended
 36 x ~35.7 MB of KV -- far more than the 256 MB Infinity Cache -- straight
 from HBM, as a real decode step does.  The prefill section times the
 prefill path (pa_write_kv of 4 x 1024 new tokens + pa_prefill, two of the
-sequences after 512 cached tokens) over the same 36-layer stack.
+sequences after 512 cached tokens) over the same 36-layer stack, and the
+verify section the pass that checks drafted blocks (4 sequences x 8 query
+tokens: pa_write_kv + pa_decode_multi + pa_decode_multi_reduce per layer).
 
 Prints ONE JSON line.  `value` = whole-step KV bytes / step time.  The
 roofline object covers the decode kernel: algorithmic KV bytes per launch /
@@ -43,6 +45,7 @@ def parse():
     ap.add_argument("--layers", type=int, default=36)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-verify", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     return ap.parse_args()
 
@@ -221,10 +224,11 @@ def main():
                               "note": "same step captured once as a HIP graph and replayed"},
     }
 
+    del kc, vc
+    torch.cuda.empty_cache()
+
     # ---------------- prefill: Qwen3-4B shape, 4 x 1024 ----------------------
     if not args.no_prefill:
-        del kc, vc
-        torch.cuda.empty_cache()
         pc = workloads.qwen3_4b_prefill(poison=False)
         pkc = [pc.k_cache.to(dev)]
         pvc = [pc.v_cache.to(dev)]
@@ -291,12 +295,93 @@ def main():
                          "kernel": "prefill_kernel<128>", "avg_launch_us": round(pf_us, 3)},
         }
         del pkc, pvc
+        torch.cuda.empty_cache()
+
+    # ---------------- verify: Qwen3-4B shape, batch 4, T = 8 -----------------
+    if not args.no_verify:
+        result["verify"] = verify_leg(args, lib, dev, gen, stream, L)
 
     # ---------------- CPU baseline: the oracle on a bounded sample -----------
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
+
+
+def verify_leg(args, lib, dev, gen, stream, L):
+    """The pass that checks a drafted block ("Qwen3-4B / 8B / 32B", section
+    DSpark Speculative Decoding): per layer the T = 8 query tokens' K/V are
+    appended (pa_write_kv, 32 tokens), then pa_decode_multi and
+    pa_decode_multi_reduce run over contexts of 1024-1152 tokens.  Reported
+    as KV GB/s like the decode step."""
+    import torch
+    import paged_kv_gqa_write_amd as pa
+    import workloads
+    case = workloads.qwen3_4b_verify(batch=4, poison=False)
+    B, T, hq, hkv, d = case.batch, case.query_len, case.num_q_heads, case.num_kv_heads, case.head_dim
+    nb = case.num_blocks
+    kc = [case.k_cache.to(dev)]
+    vc = [case.v_cache.to(dev)]
+    for _ in range(1, L):
+        kc.append(torch.randn(kc[0].shape, generator=gen, device=dev).to(torch.bfloat16))
+        vc.append(torch.randn(vc[0].shape, generator=gen, device=dev).to(torch.bfloat16))
+    q = case.q.to(dev)
+    k_new, v_new, slots = case.k_new.to(dev), case.v_new.to(dev), case.slot_mapping.to(dev)
+    bt, ctx = case.block_tables.to(dev), case.context_lens.to(dev)
+    ps, npart = pa.decode_split_plan(B, hkv, int(case.context_lens.max()))
+    out = torch.empty(B, T, hq, d, dtype=torch.bfloat16, device=dev)
+    part_out = torch.empty(B, T, hq, npart, d, dtype=torch.float32, device=dev)
+    part_lse = torch.empty(B, T, hq, npart, dtype=torch.float32, device=dev)
+    sptr = stream.cuda_stream
+
+    def multi(i):
+        return lib.pa_decode_multi(out.data_ptr(), part_out.data_ptr(), part_lse.data_ptr(),
+                                   q.data_ptr(), kc[i].data_ptr(), vc[i].data_ptr(),
+                                   bt.data_ptr(), ctx.data_ptr(), B, T, hq, hkv, d, 16, nb,
+                                   bt.shape[1], ps, npart, case.scale, sptr)
+
+    def layer(i):
+        st = lib.pa_write_kv(k_new.data_ptr(), v_new.data_ptr(), slots.data_ptr(),
+                             kc[i].data_ptr(), vc[i].data_ptr(), B * T, hkv, d, 16, nb, sptr)
+        st |= multi(i)
+        if npart > 1:
+            st |= lib.pa_decode_multi_reduce(out.data_ptr(), part_out.data_ptr(),
+                                             part_lse.data_ptr(), ctx.data_ptr(), B, T, hq, d,
+                                             ps, npart, sptr)
+        if st != 0:
+            raise RuntimeError("verify launch failed")
+
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    for _ in range(args.warmup):
+        for i in range(L):
+            layer(i)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        for i in range(L):
+            layer(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    t0.record(stream)
+    for _ in range(args.steps):
+        for i in range(L):
+            multi(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    k_us = t0.elapsed_time(t1) / (args.steps * L) * 1e3
+    kvb = case.kv_bytes()
+    del kc, vc
+    torch.cuda.empty_cache()
+    return {"workload": f"{case.name}: 4 sequences x 8 query tokens (last accepted + 7 drafted), "
+                        "context 1024-1152, 32/8 heads, head_dim 128, 36 layers "
+                        "(write_kv + decode_multi + reduce per layer)",
+            "value": round(kvb * L / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "ms_per_step": round(ms, 4), "partition_size": ps, "num_partitions": npart,
+            "kernel_avg_launch_us": round(k_us, 3),
+            "kernel_GBps": round(kvb / (k_us * 1e-6) / 1e9, 1),
+            "kernel_frac_of_hbm_peak": round(kvb / (k_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
 def cpu_baseline(seconds):
