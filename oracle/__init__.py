@@ -9,6 +9,7 @@ from .paged_attention import (  # noqa: F401
     bf16_ulp,
     causal_visible,
     combine_partials,
+    copy_blocks,
     decode,
     decode_multi,
     decode_multi_partials,

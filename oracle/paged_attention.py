@@ -24,6 +24,12 @@ What is computed (the pages print no formula; this is the plainest reading):
     sits at position ctx - T + t and sees keys 0..ctx - T + t (causal within
     the block, full over the cached context), exactly as those tokens would
     be computed as a prefill whose cached prefix is the first ctx - T tokens.
+  * Same page, section KV Offload: sealed KV blocks are restored from a
+    host tier instead of recomputing the prefill.  Read as a block-granular
+    copy: destination block d_i of a pool (or of a packed buffer of blocks)
+    receives source block s_i, K and V of every KV head, bit for bit; a copy
+    that names a block outside either side is skipped.  The same copy makes a
+    private duplicate of a shared prefix block inside one pool.
   * Attention itself is scaled dot-product softmax attention:
       z_j = scale * <q, k_j>,   w_j = exp(z_j) / sum_i exp(z_i),
       out = sum_j w_j v_j,
@@ -336,3 +342,22 @@ def decode_multi_partials(q, k_cache, v_cache, block_tables, context_lens, scale
                     part_out[s, t, h, p] = (e @ V[lo:hi, g, :]) / np.sum(e)
                     part_lse[s, t, h, p] = m + np.log(np.sum(e))
     return part_out, part_lse
+
+
+def copy_blocks(dst_k, dst_v, dst_ids, src_k, src_v, src_ids, num_copies):
+    """Block-granular KV copy.  For i in [0, num_copies): destination block
+    dst_ids[i] (block i when dst_ids is None) receives source block
+    src_ids[i] (block i when src_ids is None) -- the whole [Hkv, 16, D] K
+    tile and [Hkv, D, 16] V tile, bit for bit.  A copy whose source or
+    destination id lies outside its pool is skipped.  Returns new destination
+    pools (uint16 bit patterns)."""
+    dk = np.array(dst_k, copy=True)
+    dv = np.array(dst_v, copy=True)
+    for i in range(num_copies):
+        s = i if src_ids is None else int(src_ids[i])
+        d = i if dst_ids is None else int(dst_ids[i])
+        if not (0 <= s < src_k.shape[0] and 0 <= d < dk.shape[0]):
+            continue
+        dk[d] = src_k[s]
+        dv[d] = src_v[s]
+    return dk, dv

@@ -481,6 +481,67 @@ def pin_decode_multi_invariants():
                     assert abs(pl[s, t, h, p] - lse) < 1e-12
 
 
+# ---------------------------------------------------------------------------
+# Block-granular copy (host-tier restore / save, duplicating a shared block)
+# ---------------------------------------------------------------------------
+
+def pin_copy_blocks_elementwise():
+    """Element by element: destination block d receives source block s for
+    every (head, row, d) of K and (head, d, offset) of V; skipped and
+    untouched blocks keep their bits; None ids mean blocks 0..n-1."""
+    gen = torch.Generator().manual_seed(61)
+    hkv, d = 3, 5
+    sk = random_bf16_bits(gen, (7, hkv, 16, d))
+    sv = random_bf16_bits(gen, (7, hkv, d, 16))
+    dk0 = random_bf16_bits(gen, (9, hkv, 16, d))
+    dv0 = random_bf16_bits(gen, (9, hkv, d, 16))
+    src = np.array([6, 0, 3, 9, 2, -1], dtype=np.int32)
+    dst = np.array([1, 8, 4, 2, 12, 5], dtype=np.int32)
+    dk, dv = oracle.copy_blocks(dk0, dv0, dst, sk, sv, src, 6)
+    ek, ev = dk0.copy(), dv0.copy()
+    for i in range(6):
+        if not (0 <= src[i] < 7 and 0 <= dst[i] < 9):
+            continue
+        for g in range(hkv):
+            for r in range(16):
+                for e in range(d):
+                    ek[dst[i], g, r, e] = sk[src[i], g, r, e]
+                    ev[dst[i], g, e, r] = sv[src[i], g, e, r]
+    assert np.array_equal(dk, ek) and np.array_equal(dv, ev)
+    assert np.array_equal(dk[[0, 2, 3, 5, 6, 7]], dk0[[0, 2, 3, 5, 6, 7]])
+    pk, pv = oracle.copy_blocks(np.zeros((3, hkv, 16, d), np.uint16),
+                                np.zeros((3, hkv, d, 16), np.uint16), None, sk, sv,
+                                np.array([5, 1, 4], dtype=np.int32), 3)
+    assert np.array_equal(pk, sk[[5, 1, 4]]) and np.array_equal(pv, sv[[5, 1, 4]])
+    rk, rv = oracle.copy_blocks(dk0, dv0, np.array([0, 7], dtype=np.int32), pk, pv, None, 2)
+    assert np.array_equal(rk[0], sk[5]) and np.array_equal(rk[7], sk[1])
+    assert np.array_equal(rv[0], sv[5]) and np.array_equal(rv[7], sv[1])
+
+
+def pin_copy_blocks_save_restore_round_trip():
+    """Saving a sequence's blocks to a packed buffer and restoring them into
+    other blocks of a fresh pool gives the same attention through the new
+    table, bit for bit (the host-tier restore replaces a prefill)."""
+    from workloads import make_decode_case
+    c = make_decode_case("rt", context_lens=[37, 50], num_q_heads=4, num_kv_heads=2,
+                         head_dim=8, num_blocks=16, seed=19, poison=False)
+    q, kc, vc, bt, ctx = _case_bits(c)
+    base = oracle.decode(q, kc, vc, bt, ctx, c.scale, 4, 2)
+    used = [int(b) for b in bt.reshape(-1) if b >= 0]
+    n = len(used)
+    hk, hv = oracle.copy_blocks(np.zeros((n,) + kc.shape[1:], np.uint16),
+                                np.zeros((n,) + vc.shape[1:], np.uint16), None, kc, vc,
+                                np.array(used, dtype=np.int32), n)
+    gen = torch.Generator().manual_seed(20)
+    fresh = torch.randperm(40, generator=gen).numpy()[:n].astype(np.int32)
+    nk = random_bf16_bits(gen, (40,) + kc.shape[1:])
+    nv = random_bf16_bits(gen, (40,) + vc.shape[1:])
+    nk, nv = oracle.copy_blocks(nk, nv, fresh, hk, hv, None, n)
+    remap = dict(zip(used, fresh))
+    bt2 = np.where(bt >= 0, np.vectorize(lambda b: remap.get(int(b), -1))(bt), -1).astype(np.int32)
+    assert np.array_equal(oracle.decode(q, nk, nv, bt2, ctx, c.scale, 4, 2), base)
+
+
 ALL_PINS = [
     pin_golden_cases,
     pin_bf16_conversions,
@@ -497,4 +558,6 @@ ALL_PINS = [
     pin_brute_decode_multi,
     pin_closed_forms_decode_multi,
     pin_decode_multi_invariants,
+    pin_copy_blocks_elementwise,
+    pin_copy_blocks_save_restore_round_trip,
 ]

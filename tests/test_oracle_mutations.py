@@ -45,6 +45,11 @@ MUTATIONS = {
     "multi_tokens_reversed": ("out[s] = attend(qf[s], K, V, scale, visible",
                               "out[s] = attend(qf[s][::-1], K, V, scale, visible"),
     "multi_short_context_not_nan": ("            out[s] = np.nan\n", "            pass\n"),
+    "copy_ids_swapped": ("s = i if src_ids is None else int(src_ids[i])\n        d = i if dst_ids is None else int(dst_ids[i])",
+                         "d = i if src_ids is None else int(src_ids[i])\n        s = i if dst_ids is None else int(dst_ids[i])"),
+    "copy_v_from_k": ("dv[d] = src_v[s]", "dv[d] = np.swapaxes(src_k[s], 1, 2)"),
+    "copy_skip_check_dropped": ("if not (0 <= s < src_k.shape[0] and 0 <= d < dk.shape[0]):",
+                                "if not (-src_k.shape[0] <= s < src_k.shape[0] and 0 <= d < dk.shape[0]):"),
     "multi_partials_ignore_causal": ("lo, hi = p * partition_size, min(int(vis[t]), (p + 1) * partition_size)",
                                      "lo, hi = p * partition_size, min(n, (p + 1) * partition_size)"),
 }
