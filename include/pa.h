@@ -230,6 +230,40 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
                float scale, void* stream);
 
 /*
+ * pa_copy_blocks -- block-granular KV copy: restoring sealed blocks from a
+ * host tier instead of recomputing their prefill, saving them to it
+ * ("Qwen3-4B / 8B / 32B", section KV Offload), and duplicating a shared
+ * block inside one pool.
+ *
+ * For every i in [0, num_copies):
+ *   destination block dst_block_ids[i] := source block src_block_ids[i]
+ * for both pools (the whole [Hkv, 16, D] K tile and [Hkv, D, 16] V tile,
+ * bit for bit).  A NULL id array means "block i" for copy i, i.e. a packed
+ * run of num_copies blocks in the pool layout.  A copy whose source id is
+ * outside [0, src_num_blocks) or whose destination id is outside
+ * [0, dst_num_blocks) is skipped.  Two copies with the same destination
+ * race; a block that is both a source and a destination in one call gives
+ * an unspecified result.
+ *
+ *   dst_k_cache, dst_v_cache   destination pools [dst_num_blocks, ...]: device
+ *                  memory of the current device or pinned host memory
+ *                  (hipHostMalloc); 16-byte aligned
+ *   src_k_cache, src_v_cache   source pools [src_num_blocks, ...], same rules
+ *   dst_block_ids, src_block_ids   int32 [num_copies] in device or pinned
+ *                  host memory, or NULL
+ * Pinned host memory is read or written by the kernel over the host link
+ * through its device mapping (no staging copy).  Pageable host memory or
+ * another device's memory is PA_ERR_INVALID_ARG (checked on the host before
+ * anything is enqueued).
+ */
+int pa_copy_blocks(void* dst_k_cache, void* dst_v_cache, int64_t dst_num_blocks,
+                   const int32_t* dst_block_ids,
+                   const void* src_k_cache, const void* src_v_cache, int64_t src_num_blocks,
+                   const int32_t* src_block_ids,
+                   int32_t num_copies, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t block_size, void* stream);
+
+/*
  * pa_decode_split_plan -- host-only helper: a partition size (multiple of
  * 16) and count for pa_decode that give the GPU enough independent work
  * items while covering max_context_len.  Writes *partition_size and

@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "PAError", "load_library", "library_path", "write_kv", "decode", "decode_partials",
     "decode_reduce", "decode_multi", "decode_multi_partials", "decode_multi_reduce", "prefill",
-    "decode_split_plan", "status_string", "EXPORTED_SYMBOLS",
+    "copy_blocks", "decode_split_plan", "status_string", "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -44,6 +44,8 @@ _SIGNATURES = {
                                               _i32, _vp]),
     "pa_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                   _i32, _i32, _i32, _i64, _i32, _f32, _vp]),
+    "pa_copy_blocks": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _vp, _i64, _vp, _i32, _i32, _i32,
+                                      _i32, _vp]),
     "pa_decode_split_plan": (ctypes.c_int, [_i32, _i32, _i32, _i32, _pi32, _pi32]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
@@ -330,3 +332,53 @@ def decode_multi(q, k_cache, v_cache, block_tables, context_lens, scale, *,
                                                scale, partition_size, num_partitions, part_out,
                                                part_lse)
     return decode_multi_reduce(part_out, part_lse, context_lens, partition_size, out=out)
+
+
+# ---------------------------------------------------------------------------
+# Block-granular copy (host-tier restore / save, duplicating a shared block)
+# ---------------------------------------------------------------------------
+
+def _reachable(t: torch.Tensor, name: str, dtype, ndim: int):
+    """A GPU tensor or a pinned host tensor (the kernel reaches pinned host
+    memory through its device mapping); contiguous, of the given dtype."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not (t.is_cuda or t.is_pinned()):
+        raise ValueError(f"{name} must be a GPU tensor or pinned host memory")
+
+
+def copy_blocks(dst_k, dst_v, src_k, src_v, dst_ids=None, src_ids=None, num_copies=None):
+    """Copy whole blocks: dst block dst_ids[i] := src block src_ids[i] for K
+    and V (ids None: blocks 0..n-1, a packed run).  Either side may be a GPU
+    pool or pinned host memory in the pool layout.  Runs on the current
+    stream of the GPU in use."""
+    for t, n in ((dst_k, "dst_k"), (src_k, "src_k")):
+        _reachable(t, n, torch.bfloat16, 4)
+    for t, n in ((dst_v, "dst_v"), (src_v, "src_v")):
+        _reachable(t, n, torch.bfloat16, 4)
+    dnb, hkv, bs, d = dst_k.shape
+    snb = src_k.shape[0]
+    if bs != BLOCK_SIZE or tuple(src_k.shape[1:]) != (hkv, bs, d) \
+            or tuple(dst_v.shape) != (dnb, hkv, d, bs) or tuple(src_v.shape) != (snb, hkv, d, bs):
+        raise ValueError("pools must be K [NB, Hkv, 16, D] and V [NB, Hkv, D, 16] on both sides")
+    for t, n in ((dst_ids, "dst_ids"), (src_ids, "src_ids")):
+        if t is not None:
+            _reachable(t, n, torch.int32, 1)
+    if num_copies is None:
+        given = [t.shape[0] for t in (dst_ids, src_ids) if t is not None]
+        num_copies = given[0] if given else min(dnb, snb)
+    for t, n in ((dst_ids, "dst_ids"), (src_ids, "src_ids")):
+        if t is not None and t.shape[0] < num_copies:
+            raise ValueError(f"{n} holds fewer than num_copies ids")
+    dev = next((t.device for t in (dst_k, src_k) if t.is_cuda), torch.device("cuda"))
+    ptr = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
+    st = load_library().pa_copy_blocks(dst_k.data_ptr(), dst_v.data_ptr(), dnb, ptr(dst_ids),
+                                       src_k.data_ptr(), src_v.data_ptr(), snb, ptr(src_ids),
+                                       int(num_copies), hkv, d, BLOCK_SIZE, _stream(dev))
+    _check(st, "pa_copy_blocks")

@@ -28,6 +28,37 @@ int check_heads(int32_t hq, int32_t hkv, int32_t d, int32_t bs) {
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// The address under which the kernels may access a caller's buffer: device
+// memory of the current device as it is, pinned host memory through its
+// device mapping.  Pageable host memory, another device's memory and
+// unknown pointers are rejected, so no kernel is ever handed an address it
+// cannot reach.  A failed query leaves an error in HIP's last-error slot;
+// it is cleared so that it cannot surface from a later, unrelated call.
+int device_address(const void* p, const void** out) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return PA_ERR_INVALID_ARG;
+  }
+  if (a.type == hipMemoryTypeDevice) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != a.device) {
+      (void)hipGetLastError();
+      return PA_ERR_INVALID_ARG;
+    }
+    *out = p;
+    return PA_OK;
+  }
+  if (a.type == hipMemoryTypeHost && a.devicePointer != nullptr && a.hostPointer != nullptr) {
+    // Offset of p inside the mapping, whether the query reports the
+    // mapping's base or p itself.
+    const char* host = static_cast<const char*>(a.hostPointer);
+    *out = static_cast<const char*>(a.devicePointer) + (static_cast<const char*>(p) - host);
+    return PA_OK;
+  }
+  return PA_ERR_INVALID_ARG;
+}
+
 }  // namespace
 
 extern "C" {
@@ -129,6 +160,35 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
   return pa::launch_prefill(out, q, k_cache, v_cache, block_tables, cu_seqlens, prefix_lens,
                             num_seqs, total_q, max_q_len, num_q_heads, num_kv_heads, head_dim,
                             num_blocks, max_blocks_per_seq, scale, as_stream(stream));
+}
+
+int pa_copy_blocks(void* dst_k_cache, void* dst_v_cache, int64_t dst_num_blocks,
+                   const int32_t* dst_block_ids, const void* src_k_cache,
+                   const void* src_v_cache, int64_t src_num_blocks,
+                   const int32_t* src_block_ids, int32_t num_copies, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t block_size, void* stream) {
+  if (num_copies < 0 || num_kv_heads <= 0 || dst_num_blocks < 0 || src_num_blocks < 0)
+    return PA_ERR_INVALID_ARG;
+  if (!supported_head_dim(head_dim) || block_size != kBlockSize) return PA_ERR_UNSUPPORTED;
+  if (num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
+  if (2 * (int64_t)num_copies > kMaxGrid) return PA_ERR_UNSUPPORTED;
+  if (num_copies == 0) return PA_OK;
+  if (!dst_k_cache || !dst_v_cache || !src_k_cache || !src_v_cache) return PA_ERR_INVALID_ARG;
+  const void* bufs[4] = {dst_k_cache, dst_v_cache, src_k_cache, src_v_cache};
+  for (const void* b : bufs)
+    if (reinterpret_cast<uintptr_t>(b) % 16 != 0) return PA_ERR_INVALID_ARG;
+  const void *dk, *dv, *sk, *sv, *di = nullptr, *si = nullptr;
+  int st;
+  if ((st = device_address(dst_k_cache, &dk)) != PA_OK) return st;
+  if ((st = device_address(dst_v_cache, &dv)) != PA_OK) return st;
+  if ((st = device_address(src_k_cache, &sk)) != PA_OK) return st;
+  if ((st = device_address(src_v_cache, &sv)) != PA_OK) return st;
+  if (dst_block_ids && (st = device_address(dst_block_ids, &di)) != PA_OK) return st;
+  if (src_block_ids && (st = device_address(src_block_ids, &si)) != PA_OK) return st;
+  return pa::launch_copy_blocks(const_cast<void*>(dk), const_cast<void*>(dv), dst_num_blocks,
+                                static_cast<const int32_t*>(di), sk, sv, src_num_blocks,
+                                static_cast<const int32_t*>(si), num_copies, num_kv_heads,
+                                head_dim, as_stream(stream));
 }
 
 int pa_decode_split_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,

@@ -31,4 +31,11 @@ int launch_prefill(void* out, const void* q, const void* k_cache, const void* v_
                    int num_q_heads, int num_kv_heads, int head_dim, int64_t num_blocks,
                    int max_blocks_per_seq, float scale, hipStream_t stream);
 
+// Pointers are device addresses (pinned host memory already translated);
+// ids may be null (block i for copy i).
+int launch_copy_blocks(void* dst_k, void* dst_v, int64_t dst_num_blocks, const int32_t* dst_ids,
+                       const void* src_k, const void* src_v, int64_t src_num_blocks,
+                       const int32_t* src_ids, int num_copies, int num_kv_heads, int head_dim,
+                       hipStream_t stream);
+
 }  // namespace pa

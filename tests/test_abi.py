@@ -31,8 +31,8 @@ def lib():
 def test_header_declares_the_boundary():
     assert header_functions() == sorted(["pa_write_kv", "pa_decode", "pa_decode_reduce",
                                          "pa_decode_multi", "pa_decode_multi_reduce",
-                                         "pa_prefill", "pa_decode_split_plan",
-                                         "pa_status_string"])
+                                         "pa_prefill", "pa_copy_blocks",
+                                         "pa_decode_split_plan", "pa_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -186,6 +186,31 @@ def test_decode_multi_reduce_validation(lib):
     assert _multi_reduce(lib, pl=None) == INVALID
     assert _multi_reduce(lib, B=0x1000000, T=16, hq=256) == UNSUPPORTED
     assert _multi_reduce(lib, B=0, out=None, po=None, pl=None) == OK
+
+
+def _copy(lib, **kw):
+    a = dict(dk=FAKE, dv=FAKE, dnb=4096, di=FAKE, sk=FAKE, sv=FAKE, snb=1024, si=None, n=1024,
+             hkv=8, d=128, bs=16)
+    a.update(kw)
+    return lib.pa_copy_blocks(a["dk"], a["dv"], a["dnb"], a["di"], a["sk"], a["sv"], a["snb"],
+                              a["si"], a["n"], a["hkv"], a["d"], a["bs"], None)
+
+
+def test_copy_blocks_validation(lib):
+    assert _copy(lib, n=-1) == INVALID
+    assert _copy(lib, hkv=0) == INVALID
+    assert _copy(lib, dnb=-1) == INVALID
+    assert _copy(lib, snb=-2) == INVALID
+    assert _copy(lib, d=100) == UNSUPPORTED
+    assert _copy(lib, bs=32) == UNSUPPORTED
+    assert _copy(lib, hkv=70000) == UNSUPPORTED
+    assert _copy(lib, n=0x40000000) == UNSUPPORTED        # grid of 2n workgroups too large
+    assert _copy(lib, dk=None) == INVALID
+    assert _copy(lib, sv=None) == INVALID
+    assert _copy(lib, dk=FAKE + 8) == INVALID             # pools must be 16-byte aligned
+    assert _copy(lib, sv=FAKE + 4) == INVALID
+    # zero copies is a no-op that touches nothing
+    assert _copy(lib, n=0, dk=None, dv=None, sk=None, sv=None, di=None) == OK
 
 
 def _prefill(lib, **kw):
