@@ -46,6 +46,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-verify", action="store_true")
+    ap.add_argument("--no-restore", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     return ap.parse_args()
 
@@ -301,6 +302,10 @@ def main():
     if not args.no_verify:
         result["verify"] = verify_leg(args, lib, dev, gen, stream, L)
 
+    # ---------------- block copy: host-tier restore of a 16k-token prefix ----
+    if not args.no_restore:
+        result["kv_restore"] = restore_leg(args, lib, dev, stream)
+
     # ---------------- CPU baseline: the oracle on a bounded sample -----------
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
@@ -382,6 +387,73 @@ def verify_leg(args, lib, dev, gen, stream, L):
             "kernel_avg_launch_us": round(k_us, 3),
             "kernel_GBps": round(kvb / (k_us * 1e-6) / 1e9, 1),
             "kernel_frac_of_hbm_peak": round(kvb / (k_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
+def restore_leg(args, lib, dev, stream):
+    """Host-tier restore ("Qwen3-4B / 8B / 32B", section KV Offload): the
+    1024 sealed blocks of a 16384-token Qwen3-4B prefix, per layer, copied by
+    pa_copy_blocks from packed pinned host buffers into scattered pool blocks
+    (the kernel reads host memory directly).  8 host buffers (64 MiB each)
+    rotate over the layers.  Also: the same 1024 blocks duplicated inside
+    the device pool (HBM read + write), and a plain 64 MiB host-to-device
+    DMA copy of one buffer for the host link's reference rate."""
+    import torch
+    hkv, d, n, nb, nh = 8, 128, 1024, 4096, 8
+    blk = hkv * 16 * d * 2
+    kc = torch.empty((nb, hkv, 16, d), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty((nb, hkv, d, 16), dtype=torch.bfloat16, device=dev)
+    hk = [torch.zeros((n, hkv, 16, d), dtype=torch.bfloat16, pin_memory=True) for _ in range(nh)]
+    hv = [torch.zeros((n, hkv, d, 16), dtype=torch.bfloat16, pin_memory=True) for _ in range(nh)]
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    perm = torch.randperm(nb, generator=g, device=dev).to(torch.int32)
+    dst, cow_src, cow_dst = perm[:n].contiguous(), perm[n:2 * n].contiguous(), perm[2 * n:3 * n].contiguous()
+    stage_k = torch.empty_like(kc[:n])
+    sptr = stream.cuda_stream
+
+    def restore(i):
+        if lib.pa_copy_blocks(kc.data_ptr(), vc.data_ptr(), nb, dst.data_ptr(), hk[i % nh].data_ptr(),
+                              hv[i % nh].data_ptr(), n, None, n, hkv, d, 16, sptr) != 0:
+            raise RuntimeError("restore launch failed")
+
+    def cow(i):
+        if lib.pa_copy_blocks(kc.data_ptr(), vc.data_ptr(), nb, cow_dst.data_ptr(), kc.data_ptr(),
+                              vc.data_ptr(), nb, cow_src.data_ptr(), n, hkv, d, 16, sptr) != 0:
+            raise RuntimeError("copy launch failed")
+
+    def h2d(i):
+        stage_k.copy_(hk[i % nh], non_blocking=True)
+
+    def timed(fn, count):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        for i in range(nh):
+            fn(i)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for i in range(count):
+            fn(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / count * 1e3
+
+    layers = 36
+    reps = max(1, args.steps // 4)
+    r_us = timed(restore, layers * reps)
+    c_us = timed(cow, layers * reps)
+    h_us = timed(h2d, layers * reps)
+    moved = 2 * n * blk
+    del kc, vc, hk, hv, stage_k
+    torch.cuda.empty_cache()
+    return {"workload": "restore of a 16384-token Qwen3-4B prefix from pinned host memory: 1024 blocks "
+                        "x 36 layers, 64 MiB per layer, into scattered pool blocks (pa_copy_blocks)",
+            "ms_per_prefix": round(r_us * layers / 1e3, 3),
+            "host_link_GBps": round(moved / r_us / 1e3, 1),
+            "h2d_dma_copy_GBps": round(blk * n / h_us / 1e3, 1),
+            "in_pool_copy": {"us_per_layer": round(c_us, 2),
+                             "roofline": {"bound": "hbm", "achieved": round(2 * moved / c_us / 1e3, 1),
+                                          "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                          "frac": round(2 * moved / c_us / 1e3 / HBM_PEAK_GBPS, 4)}}}
 
 
 def cpu_baseline(seconds):
