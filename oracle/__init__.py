@@ -22,3 +22,4 @@ from .paged_attention import (  # noqa: F401
     softmax_rows,
     write_kv,
 )
+from .prefix_cache import PrefixCache  # noqa: F401

@@ -542,6 +542,88 @@ def pin_copy_blocks_save_restore_round_trip():
     assert np.array_equal(oracle.decode(q, nk, nv, bt2, ctx, c.scale, 4, 2), base)
 
 
+# ---------------------------------------------------------------------------
+# Prefix-block matching (host side of the prefix cache)
+# ---------------------------------------------------------------------------
+
+def _toks(*parts):
+    out = []
+    for p in parts:
+        out += list(p)
+    return out
+
+
+def pin_prefix_cache_scenario():
+    """A scripted sequence of registrations, lookups and removals whose
+    results follow by hand from the definition (full blocks only, a block is
+    identified by its whole prefix, first sealed copy kept, removal drops
+    everything extending the block, reuse of a block id drops its old
+    entry, invalid calls change nothing)."""
+    a0, a1, a2 = list(range(100, 116)), list(range(200, 216)), list(range(300, 308))
+    x0, y1, z2 = list(range(400, 416)), list(range(500, 516)), list(range(600, 616))
+    A = _toks(a0, a1, a2)                 # 40 tokens: 2 full blocks + 8
+    B = _toks(a0, a1, z2, [7, 7, 7, 7])   # 52 tokens: 3 full blocks
+    C = _toks(x0, a1)                     # A's second block after another first block
+    D = _toks(a0, y1)
+    pc = oracle.PrefixCache(100)
+    assert pc.match(A) == []
+    assert pc.insert(A, [10, 11]) == 2
+    assert pc.match(A) == [10, 11] and len(pc) == 2
+    assert pc.match(A[:31]) == [10]       # the partial second block never matches
+    assert pc.match(B) == [10, 11]
+    assert pc.insert(B, [10, 11, 12]) == 1
+    assert pc.match(B) == [10, 11, 12]
+    assert pc.match(C) == []              # same block contents, different position in the prefix
+    assert pc.match(D) == [10]
+    assert pc.insert(B, [90, 91, 92]) == 0  # already cached: first copies kept
+    assert pc.match(B) == [10, 11, 12]
+    assert pc.remove(11) == 2             # A's block 1 and B's block 2, which extends it
+    assert pc.match(B) == [10] and pc.match(A) == [10] and len(pc) == 1
+    assert pc.insert(D, [99, 10]) is None  # 10 already holds D's own block 0
+    assert pc.insert(D, [10, 13, 13]) is not None  # D has 2 full blocks: the third id is unused
+    assert pc.match(D) == [10, 13]
+    assert pc.insert(C, [13, 20]) == 2    # block 13 reused: D's entry for it goes first
+    assert pc.match(D) == [10] and pc.match(C) == [13, 20] and len(pc) == 3
+    assert pc.insert(A, [5, 6, 6]) is not None
+    assert pc.match(A) == [10, 6]
+    assert pc.insert(B, [1, 2, 2]) == 1   # blocks 0, 1 cached (10, 6): only id 2 for block 2
+    assert pc.insert(_toks(x0, y1, z2), [30, 30, 31]) == 2     # block 0 cached: its id unused
+    assert pc.insert(_toks(y1, x0, z2), [32, 32, 33]) is None  # duplicate ids to register
+    assert pc.insert(_toks(z2, y1, x0), [40, -1, 41]) == 1     # a negative id stops there
+    assert pc.match(_toks(z2, y1, x0)) == [40]
+    small = oracle.PrefixCache(3)
+    assert small.insert(A, [1, 2]) == 2
+    assert small.insert(_toks(x0, y1, z2), [5, 6, 7]) == 1      # full after one more
+    assert small.insert(_toks(x0, y1, z2), [5, 2, 7]) == 1      # reusing 2 frees A's entry
+    assert small.match(_toks(x0, y1, z2)) == [5, 2] and small.match(A) == [1]
+
+
+def pin_prefix_cache_invariants():
+    """Random sequences: a registered sequence matches its own ids; changing
+    one token at position p leaves exactly the p // 16 leading blocks
+    matched; removing block j of a sequence leaves its j leading blocks."""
+    gen = torch.Generator().manual_seed(55)
+    pc = oracle.PrefixCache(10_000)
+    next_id = 0
+    for trial in range(40):
+        n = int(torch.randint(0, 200, (1,), generator=gen))
+        toks = torch.randint(0, 50, (n,), generator=gen).tolist()
+        nb = n // 16
+        ids = list(range(next_id, next_id + nb))
+        next_id += nb
+        got = pc.insert(toks, ids)
+        m = pc.match(toks)
+        assert len(m) == nb and got == sum(1 for b in m if b in ids)
+        if nb:
+            p = int(torch.randint(0, n, (1,), generator=gen))
+            alt = list(toks)
+            alt[p] += 1000
+            assert pc.match(alt) == m[:p // 16]
+            j = int(torch.randint(0, nb, (1,), generator=gen))
+            pc.remove(m[j])
+            assert pc.match(toks) == m[:j]
+
+
 ALL_PINS = [
     pin_golden_cases,
     pin_bf16_conversions,
@@ -560,4 +642,6 @@ ALL_PINS = [
     pin_decode_multi_invariants,
     pin_copy_blocks_elementwise,
     pin_copy_blocks_save_restore_round_trip,
+    pin_prefix_cache_scenario,
+    pin_prefix_cache_invariants,
 ]

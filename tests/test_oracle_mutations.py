@@ -8,8 +8,9 @@ import pytest
 
 import _oracle_pins as pins
 
-SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                   "oracle", "paged_attention.py")
+ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+SRC = os.path.join(ORACLE_DIR, "paged_attention.py")
+PREFIX_SRC = os.path.join(ORACLE_DIR, "prefix_cache.py")
 
 MUTATIONS = {
     "interleaved_kv_heads": ("return h // (num_q_heads // num_kv_heads)",
@@ -50,23 +51,48 @@ MUTATIONS = {
     "copy_v_from_k": ("dv[d] = src_v[s]", "dv[d] = np.swapaxes(src_k[s], 1, 2)"),
     "copy_skip_check_dropped": ("if not (0 <= s < src_k.shape[0] and 0 <= d < dk.shape[0]):",
                                 "if not (-src_k.shape[0] <= s < src_k.shape[0] and 0 <= d < dk.shape[0]):"),
+    "prefix_key_ignores_earlier_blocks": (
+        PREFIX_SRC, "return tuple(int(t) for t in tokens[:BLOCK * (i + 1)])",
+        "return tuple(int(t) for t in tokens[BLOCK * i:BLOCK * (i + 1)])"),
+    "prefix_partial_block_registered": (
+        PREFIX_SRC, "n = min(len(tokens) // BLOCK, len(block_ids))",
+        "n = min((len(tokens) + BLOCK - 1) // BLOCK, len(block_ids))"),
+    "prefix_remove_keeps_descendants": (
+        PREFIX_SRC, "gone = [k for k in self.entries if any(k[:len(r)] == r for r in roots)]",
+        "gone = roots"),
+    "prefix_later_copy_replaces_first": (
+        PREFIX_SRC, "while i < n and self._key(tokens, i) in self.entries:",
+        "while i < n and self._key(tokens, i) in self.entries and False:"),
     "multi_partials_ignore_causal": ("lo, hi = p * partition_size, min(int(vis[t]), (p + 1) * partition_size)",
                                      "lo, hi = p * partition_size, min(n, (p + 1) * partition_size)"),
 }
 
 
-def _mutant(old, new):
-    with open(SRC) as f:
+def _mutant(path, old, new):
+    with open(path) as f:
         src = f.read()
     assert src.count(old) == 1, f"mutation anchor not unique/present: {old!r}"
     mod = types.ModuleType("oracle_mutant")
-    exec(compile(src.replace(old, new), SRC + " (mutant)", "exec"), mod.__dict__)
+    exec(compile(src.replace(old, new), path + " (mutant)", "exec"), mod.__dict__)
     return mod
+
+
+def _mutated_oracle(spec):
+    """The oracle package with one of its modules replaced by a mutant."""
+    import oracle
+    path, old, new = spec if len(spec) == 3 else (SRC, *spec)
+    mod = _mutant(path, old, new)
+    if path == SRC:
+        return mod
+    ns = types.SimpleNamespace(**{k: getattr(oracle, k) for k in dir(oracle)
+                                  if not k.startswith("__")})
+    ns.PrefixCache = mod.PrefixCache
+    return ns
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_mutation_is_caught(name, monkeypatch):
-    mod = _mutant(*MUTATIONS[name])
+    mod = _mutated_oracle(MUTATIONS[name])
     monkeypatch.setattr(pins, "oracle", mod)
     caught = []
     for pin in pins.ALL_PINS:
