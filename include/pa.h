@@ -1,7 +1,7 @@
 /*
  * pa.h -- grouped-query attention over a paged KV cache, for AMD Instinct
- * MI355X (gfx950).  C ABI: plain device pointers, sizes and an opaque HIP
- * stream handle; no framework types.
+ * MI355X (gfx950).  C ABI: plain pointers (device memory unless a call says
+ * otherwise), sizes and an opaque HIP stream handle; no framework types.
  *
  * What the operations compute comes from the serving pages this library
  * follows ("Qwen3-4B / 8B / 32B", section Architecture Notes; "Qwen3.5-4B /
@@ -38,10 +38,12 @@
  * Conventions shared by every call
  * ---------------------------------------------------------------------------
  *   Ownership: the caller allocates and owns every buffer, including the
- *     split-K workspace.  The library never allocates, frees or
- *     synchronises; each call only enqueues kernels on `stream` (a
- *     hipStream_t passed as void*; NULL = the default stream), so calls are
- *     asynchronous, stateless, thread-safe and may be captured in a HIP graph.
+ *     split-K workspace.  The GPU calls never allocate, free or
+ *     synchronise; each only enqueues kernels on `stream` (a hipStream_t
+ *     passed as void*; NULL = the default stream), so they are asynchronous,
+ *     stateless, thread-safe and may be captured in a HIP graph.  The
+ *     host-side prefix index (pa_prefix_index_*) is the one stateful object:
+ *     it owns the host memory it allocates and runs on the CPU only.
  *   Errors: arguments are checked on the host before anything is enqueued;
  *     on failure the call returns a negative pa_status and writes nothing.
  *     A failed kernel launch returns PA_ERR_LAUNCH.
@@ -68,7 +70,8 @@ typedef enum {
   PA_OK = 0,
   PA_ERR_INVALID_ARG = -1,  /* null pointer, negative size, inconsistent sizes */
   PA_ERR_UNSUPPORTED = -2,  /* head_dim / group / block_size outside the supported set */
-  PA_ERR_LAUNCH = -3        /* the HIP runtime rejected a kernel launch */
+  PA_ERR_LAUNCH = -3,       /* the HIP runtime rejected a kernel launch */
+  PA_ERR_NO_MEMORY = -4     /* host allocation failed (prefix index only) */
 } pa_status;
 
 /*
@@ -272,6 +275,65 @@ int pa_copy_blocks(void* dst_k_cache, void* dst_v_cache, int64_t dst_num_blocks,
 int pa_decode_split_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
                          int32_t num_compute_units,
                          int32_t* partition_size, int32_t* num_partitions);
+
+/*
+ * Prefix-block index (host only, no GPU involved): which physical KV blocks
+ * already hold the leading full blocks of a token sequence ("Qwen3-4B / 8B /
+ * 32B", Architecture Notes: prefix caching on by default, prefix matching
+ * against the GPU KV cache; section Warm Prefix-Cache TTFT).  A hit of m
+ * blocks lets pa_prefill start at prefix_len = 16*m with those blocks at the
+ * head of the sequence's block-table row.
+ *
+ * Only sealed (full, 16-token) blocks are indexed, each under the token ids
+ * of its whole prefix: block i of a sequence matches only if blocks 0..i-1
+ * match too.  Matching compares token ids exactly (hash collisions cannot
+ * return another prefix's blocks).  Tokens and block ids are host int32
+ * arrays.  The index owns the host memory it allocates (created by
+ * pa_prefix_index_create, released by pa_prefix_index_destroy).  Calls that
+ * modify an index must not overlap with any other call on it; concurrent
+ * pa_prefix_index_match calls are safe.  After PA_ERR_NO_MEMORY an index
+ * must only be destroyed.
+ */
+typedef struct pa_prefix_index pa_prefix_index;
+
+/* New empty index holding at most `capacity` (> 0) blocks; *out = NULL on error. */
+int pa_prefix_index_create(int64_t capacity, pa_prefix_index** out);
+
+/* Releases the index (NULL is a no-op). */
+void pa_prefix_index_destroy(pa_prefix_index* index);
+
+/* Number of indexed blocks (-1 for NULL). */
+int64_t pa_prefix_index_size(const pa_prefix_index* index);
+
+/*
+ * Longest cached run of leading full blocks of tokens[0..num_tokens):
+ * writes its block ids to block_ids[0..*num_matched) (room for
+ * num_tokens/16 ids).  A trailing partial block never matches.
+ */
+int pa_prefix_index_match(const pa_prefix_index* index, const int32_t* tokens,
+                          int32_t num_tokens, int32_t* block_ids, int32_t* num_matched);
+
+/*
+ * Registers the sealed blocks of a sequence: full block i of tokens lives in
+ * physical block block_ids[i] (i < min(num_tokens/16, num_block_ids)).
+ * Blocks whose prefix is already cached keep their first block (the id given
+ * for them is ignored).  The rest are added in order until a negative id or
+ * a full index.  An id already indexed under another prefix means that
+ * block was reused: its old entry and every entry extending it are dropped
+ * first.  An id that appears twice among the blocks to add, or that holds
+ * one of this sequence's cached blocks, is PA_ERR_INVALID_ARG (nothing
+ * changes).  *num_inserted = number of blocks added.
+ */
+int pa_prefix_index_insert(pa_prefix_index* index, const int32_t* tokens, int32_t num_tokens,
+                           const int32_t* block_ids, int32_t num_block_ids,
+                           int32_t* num_inserted);
+
+/*
+ * Drops the entry of physical block block_id (e.g. when the block is freed)
+ * and every entry extending it; *num_removed = entries dropped (0 if the
+ * block was not indexed).
+ */
+int pa_prefix_index_remove(pa_prefix_index* index, int32_t block_id, int32_t* num_removed);
 
 /* Host-only: a static string naming a pa_status value. */
 const char* pa_status_string(int status);

@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "PAError", "load_library", "library_path", "write_kv", "decode", "decode_partials",
     "decode_reduce", "decode_multi", "decode_multi_partials", "decode_multi_reduce", "prefill",
-    "copy_blocks", "decode_split_plan", "status_string", "EXPORTED_SYMBOLS",
+    "copy_blocks", "PrefixIndex", "decode_split_plan", "status_string", "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -27,10 +27,11 @@ _LIB_PATH = os.path.join(_PKG, "libpa.so")
 _lib = None
 
 BLOCK_SIZE = 16
-PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_LAUNCH = 0, -1, -2, -3
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_LAUNCH, PA_ERR_NO_MEMORY = 0, -1, -2, -3, -4
 
 _vp, _i32, _i64, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
 _pi32 = ctypes.POINTER(ctypes.c_int32)
+_pvp = ctypes.POINTER(ctypes.c_void_p)
 
 # name -> (restype, argtypes); mirrors include/pa.h
 _SIGNATURES = {
@@ -47,6 +48,12 @@ _SIGNATURES = {
     "pa_copy_blocks": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _vp, _i64, _vp, _i32, _i32, _i32,
                                       _i32, _vp]),
     "pa_decode_split_plan": (ctypes.c_int, [_i32, _i32, _i32, _i32, _pi32, _pi32]),
+    "pa_prefix_index_create": (ctypes.c_int, [_i64, _pvp]),
+    "pa_prefix_index_destroy": (None, [_vp]),
+    "pa_prefix_index_size": (ctypes.c_int64, [_vp]),
+    "pa_prefix_index_match": (ctypes.c_int, [_vp, _vp, _i32, _vp, _pi32]),
+    "pa_prefix_index_insert": (ctypes.c_int, [_vp, _vp, _i32, _vp, _i32, _pi32]),
+    "pa_prefix_index_remove": (ctypes.c_int, [_vp, _i32, _pi32]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
@@ -382,3 +389,62 @@ def copy_blocks(dst_k, dst_v, src_k, src_v, dst_ids=None, src_ids=None, num_copi
                                        src_k.data_ptr(), src_v.data_ptr(), snb, ptr(src_ids),
                                        int(num_copies), hkv, d, BLOCK_SIZE, _stream(dev))
     _check(st, "pa_copy_blocks")
+
+
+# ---------------------------------------------------------------------------
+# Prefix-block index (host side of the prefix cache; CPU only)
+# ---------------------------------------------------------------------------
+
+class PrefixIndex:
+    """The library's host-side prefix-block index (pa_prefix_index_*).
+
+    match(tokens) -> physical block ids of the longest cached run of leading
+    full blocks; insert(tokens, block_ids) registers a sequence's sealed
+    blocks (returns how many were added); remove(block_id) drops a block and
+    every entry extending it.  Token and block ids are int32."""
+
+    def __init__(self, capacity: int):
+        import numpy as np
+        self._np = np
+        self._lib = load_library()
+        h = ctypes.c_void_p()
+        _check(self._lib.pa_prefix_index_create(int(capacity), ctypes.byref(h)),
+               "pa_prefix_index_create")
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self._lib.pa_prefix_index_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def _tokens(self, tokens):
+        return self._np.ascontiguousarray(tokens, dtype=self._np.int32)
+
+    def match(self, tokens) -> list:
+        t = self._tokens(tokens)
+        out = self._np.empty(max(t.size // 16, 1), dtype=self._np.int32)
+        n = ctypes.c_int32(0)
+        _check(self._lib.pa_prefix_index_match(self._h, t.ctypes.data, t.size, out.ctypes.data,
+                                               ctypes.byref(n)), "pa_prefix_index_match")
+        return out[:n.value].tolist()
+
+    def insert(self, tokens, block_ids) -> int:
+        t = self._tokens(tokens)
+        b = self._np.ascontiguousarray(block_ids, dtype=self._np.int32)
+        n = ctypes.c_int32(0)
+        _check(self._lib.pa_prefix_index_insert(self._h, t.ctypes.data, t.size, b.ctypes.data,
+                                                b.size, ctypes.byref(n)),
+               "pa_prefix_index_insert")
+        return n.value
+
+    def remove(self, block_id: int) -> int:
+        n = ctypes.c_int32(0)
+        _check(self._lib.pa_prefix_index_remove(self._h, int(block_id), ctypes.byref(n)),
+               "pa_prefix_index_remove")
+        return n.value
+
+    def __len__(self) -> int:
+        return int(self._lib.pa_prefix_index_size(self._h))

@@ -17,7 +17,8 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libpa.so")
-SOURCES = ["pa_api.hip", "write_kv.hip", "decode.hip", "prefill.hip", "copy.hip"]
+SOURCES = ["pa_api.hip", "write_kv.hip", "decode.hip", "prefill.hip", "copy.hip",
+           "prefix_index.cpp"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

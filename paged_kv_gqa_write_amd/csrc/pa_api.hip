@@ -226,6 +226,7 @@ const char* pa_status_string(int status) {
     case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG: invalid argument";
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: unsupported shape";
     case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: kernel launch failed";
+    case PA_ERR_NO_MEMORY: return "PA_ERR_NO_MEMORY: host allocation failed";
     default: return "unknown pa_status";
   }
 }

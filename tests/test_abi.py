@@ -20,7 +20,8 @@ def header_functions():
     with open(HEADER) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(pa_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^(?:int|int64_t|void|const char\*)\s+(pa_\w+)\s*\(", text,
+                                 flags=re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -32,7 +33,10 @@ def test_header_declares_the_boundary():
     assert header_functions() == sorted(["pa_write_kv", "pa_decode", "pa_decode_reduce",
                                          "pa_decode_multi", "pa_decode_multi_reduce",
                                          "pa_prefill", "pa_copy_blocks",
-                                         "pa_decode_split_plan", "pa_status_string"])
+                                         "pa_decode_split_plan", "pa_status_string",
+                                         "pa_prefix_index_create", "pa_prefix_index_destroy",
+                                         "pa_prefix_index_size", "pa_prefix_index_match",
+                                         "pa_prefix_index_insert", "pa_prefix_index_remove"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -56,7 +60,7 @@ def test_missing_library_fails_loudly(tmp_path):
 
 
 def test_status_strings(lib):
-    for code in (OK, INVALID, UNSUPPORTED, pa.PA_ERR_LAUNCH):
+    for code in (OK, INVALID, UNSUPPORTED, pa.PA_ERR_LAUNCH, pa.PA_ERR_NO_MEMORY):
         s = lib.pa_status_string(code).decode()
         assert s.startswith("PA_")
     assert "unknown" in lib.pa_status_string(7).decode()
