@@ -4,10 +4,11 @@
 
 One step is one decode step of a Qwen3-4B-shaped attention stack (32 query
 heads, 8 KV heads, head_dim 128, 36 layers; "Qwen3-4B / 8B / 32B", section
-Architecture Notes): for every layer, the 8 new tokens' K/V are appended
-(pa_write_kv), then split-K decode (pa_decode) and its log-sum-exp reduce
-(pa_decode_reduce) run over contexts of 1024-1152 tokens scattered over a
-4096-block pool.  Every layer has its own pools, so a step streams
+Architecture Notes): for every layer, the 8 new tokens' K/V are appended and
+split-K decode runs over contexts of 1024-1152 tokens scattered over a
+4096-block pool (pa_decode_append: both in one kernel), then its
+log-sum-exp reduce (pa_decode_reduce).  The same step with the append as
+its own kernel (pa_write_kv + pa_decode + reduce) is reported beside it.  Every layer has its own pools, so a step streams
 36 x ~35.7 MB of KV -- far more than the 256 MB Infinity Cache -- straight
 from HBM, as a real decode step does.  The prefill section times the
 prefill path (pa_write_kv of 4 x 1024 new tokens + pa_prefill, two of the
@@ -114,13 +115,16 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
 
+    def append_decode(i, sptr=sptr):
+        return lib.pa_decode_append(out.data_ptr(), part_out.data_ptr(), part_lse.data_ptr(),
+                                    q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                                    kc[i].data_ptr(), vc[i].data_ptr(), bt.data_ptr(),
+                                    ctx.data_ptr(), B, hq, hkv, d, 16, nb, bt.shape[1], ps,
+                                    npart, case.scale, sptr)
+
     def decode_layer(i, sptr=sptr):
-        st = lib.pa_write_kv(k_new.data_ptr(), v_new.data_ptr(), slots.data_ptr(),
-                             kc[i].data_ptr(), vc[i].data_ptr(), B, hkv, d, 16, nb, sptr)
-        st |= lib.pa_decode(out.data_ptr(), part_out.data_ptr(), part_lse.data_ptr(),
-                            q.data_ptr(), kc[i].data_ptr(), vc[i].data_ptr(), bt.data_ptr(),
-                            ctx.data_ptr(), B, hq, hkv, d, 16, nb, bt.shape[1], ps, npart,
-                            case.scale, sptr)
+        # append the 8 new tokens' K/V and decode (one kernel), then the reduce
+        st = append_decode(i, sptr)
         if npart > 1:
             st |= lib.pa_decode_reduce(out.data_ptr(), part_out.data_ptr(), part_lse.data_ptr(),
                                        ctx.data_ptr(), B, hq, d, ps, npart, sptr)
@@ -168,9 +172,33 @@ def main():
     graph_ms_step = t0.elapsed_time(t1) / args.steps
     del graph
 
-    # Decode kernel alone: the same K steps' pa_decode launches issued back to
-    # back on the launch stream between one pair of HIP events (pa_write_kv
-    # and the reduce are left out), so the average is the kernel's own
+    # The same step with the append as its own kernel (pa_write_kv, then
+    # pa_decode and the reduce), for reference.
+    def split_layer(i):
+        st = lib.pa_write_kv(k_new.data_ptr(), v_new.data_ptr(), slots.data_ptr(),
+                             kc[i].data_ptr(), vc[i].data_ptr(), B, hkv, d, 16, nb, sptr)
+        st |= lib.pa_decode(out.data_ptr(), part_out.data_ptr(), part_lse.data_ptr(),
+                            q.data_ptr(), kc[i].data_ptr(), vc[i].data_ptr(), bt.data_ptr(),
+                            ctx.data_ptr(), B, hq, hkv, d, 16, nb, bt.shape[1], ps, npart,
+                            case.scale, sptr)
+        if npart > 1:
+            st |= lib.pa_decode_reduce(out.data_ptr(), part_out.data_ptr(), part_lse.data_ptr(),
+                                       ctx.data_ptr(), B, hq, d, ps, npart, sptr)
+        if st != 0:
+            raise RuntimeError("decode step launch failed")
+
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        for i in range(L):
+            split_layer(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    split_ms_step = t0.elapsed_time(t1) / args.steps
+
+    # The step's decode kernel alone (the appending form): the same K steps'
+    # launches issued back to back on the launch stream between one pair of
+    # HIP events (the reduce is left out), so the average is the kernel's own
     # duration plus the hardware's inter-dispatch gap -- what rocprofv3's
     # kernel trace reports for it, without per-launch event overhead.
     a = torch.cuda.Event(enable_timing=True)
@@ -179,9 +207,7 @@ def main():
     a.record(stream)
     for _ in range(args.steps):
         for i in range(L):
-            lib.pa_decode(out.data_ptr(), part_out.data_ptr(), part_lse.data_ptr(), q.data_ptr(),
-                          kc[i].data_ptr(), vc[i].data_ptr(), bt.data_ptr(), ctx.data_ptr(), B,
-                          hq, hkv, d, 16, nb, bt.shape[1], ps, npart, case.scale, sptr)
+            append_decode(i)
     b.record(stream)
     torch.cuda.synchronize()
     dec_us = a.elapsed_time(b) / (args.steps * L) * 1e3
@@ -189,7 +215,7 @@ def main():
     traffic = measured_traffic("decode_kernel_traffic.json", ["decode.hip", "pa_device.h"])
     roofline = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
-                "traffic": traffic, "kernel": "decode_kernel<128>",
+                "traffic": traffic, "kernel": "decode_kernel<128> (appending form)",
                 "algorithmic_bytes_per_launch": kv_bytes_layer,
                 "avg_launch_us": round(dec_us, 3)}
 
@@ -215,11 +241,16 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16 tensors shaped like the pages' workloads)",
         "config": {"workload": "qwen3_4b_decode_b8: one decode step of a 36-layer Qwen3-4B "
-                               "attention stack (write_kv + split-K decode + reduce per layer)",
+                               "attention stack (KV append + split-K decode in one kernel, then "
+                               "the reduce, per layer)",
                    "layers": L, "batch": B, "num_q_heads": hq, "num_kv_heads": hkv,
                    "head_dim": d, "block_size": 16, "context_lens": case.context_lens.tolist(),
                    "num_blocks_per_layer": nb, "partition_size": ps, "num_partitions": npart},
         "roofline": roofline,
+        "decode_step_separate_append": {
+            "ms_per_step": round(split_ms_step, 4),
+            "value": round(kv_bytes_layer * L / (split_ms_step * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "note": "same step with pa_write_kv as its own kernel before pa_decode"},
         "decode_step_graph": {"ms_per_step": round(graph_ms_step, 4),
                               "value": round(kv_bytes_layer * L / (graph_ms_step * 1e-3) / 1e9, 1),
                               "unit": "GB/s",

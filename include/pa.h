@@ -133,6 +133,33 @@ int pa_decode(void* out, float* part_out, float* part_lse,
               float scale, void* stream);
 
 /*
+ * pa_decode_append -- pa_write_kv of each sequence's new token followed by
+ * pa_decode, in one kernel: the decode step of the full-attention layers
+ * appends the token's K/V to the paged cache and attends over it
+ * ("Qwen3-4B / 8B / 32B", Architecture Notes).  For every sequence s with
+ * context_lens[s] > 0 the token at position ctx-1 (K/V = k_new[s], v_new[s])
+ * is written to the slot the block table gives that position, and the
+ * outputs are those pa_decode would produce after that write (bit for bit).
+ * The kernel does not read the new token back from the pool, so no
+ * ordering between the write and the reads is needed.  A sequence whose
+ * table entry for position ctx-1 is outside the pool (or any other invalid
+ * entry) gets NaN outputs, and that token is not written.
+ *
+ *   k_new, v_new   device, bf16 [num_seqs, Hkv, D]
+ *   k_cache, v_cache   device, pools, updated in place at the new slots
+ *   other arguments as for pa_decode (num_partitions > 1: finish with
+ *   pa_decode_reduce).
+ */
+int pa_decode_append(void* out, float* part_out, float* part_lse,
+                     const void* q, const void* k_new, const void* v_new,
+                     void* k_cache, void* v_cache,
+                     const int32_t* block_tables, const int32_t* context_lens,
+                     int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                     int32_t max_blocks_per_seq, int32_t partition_size,
+                     int32_t num_partitions, float scale, void* stream);
+
+/*
  * pa_decode_reduce -- log-sum-exp combination of pa_decode's split-K pieces:
  *   M = max_p lse_p,  w_p = e^{lse_p - M},
  *   out[s, h, :] = bf16( sum_p w_p part_out[s, h, p, :] / sum_p w_p ),

@@ -18,7 +18,7 @@ import torch
 
 __all__ = [
     "PAError", "load_library", "library_path", "write_kv", "decode", "decode_partials",
-    "decode_reduce", "decode_multi", "decode_multi_partials", "decode_multi_reduce", "prefill",
+    "decode_reduce", "decode_append", "decode_multi", "decode_multi_partials", "decode_multi_reduce", "prefill",
     "copy_blocks", "PrefixIndex", "decode_split_plan", "status_string", "EXPORTED_SYMBOLS",
 ]
 
@@ -39,6 +39,9 @@ _SIGNATURES = {
     "pa_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                  _i32, _i64, _i32, _i32, _i32, _f32, _vp]),
     "pa_decode_reduce": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pa_decode_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                        _i32, _i32, _i32, _i32, _i64, _i32, _i32, _i32, _f32,
+                                        _vp]),
     "pa_decode_multi": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                        _i32, _i32, _i32, _i64, _i32, _i32, _i32, _f32, _vp]),
     "pa_decode_multi_reduce": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -225,6 +228,50 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, *, max_contex
         return out
     part_out, part_lse = decode_partials(q, k_cache, v_cache, block_tables, context_lens, scale,
                                          partition_size, num_partitions, part_out, part_lse)
+    return decode_reduce(part_out, part_lse, context_lens, partition_size, out=out)
+
+
+def decode_append(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, *,
+                  max_context_len=None, partition_size=None, num_partitions=None, out=None,
+                  part_out=None, part_lse=None):
+    """Append each sequence's new token (k_new/v_new [B, Hkv, D], position
+    ctx-1, slot from the block table) and decode, in one kernel; with more
+    than one partition the pieces are combined by pa_decode_reduce."""
+    nb, hkv, d = _pools(k_cache, v_cache)
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_new, "k_new", torch.bfloat16, 3)
+    _need(v_new, "v_new", torch.bfloat16, 3)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    B, hq, dq = q.shape
+    if dq != d or block_tables.shape[0] != B or context_lens.shape[0] != B \
+            or tuple(k_new.shape) != (B, hkv, d) or tuple(v_new.shape) != (B, hkv, d):
+        raise ValueError("q [B, Hq, D], k_new/v_new [B, Hkv, D], block_tables [B, max_blocks], "
+                         "context_lens [B] mismatch")
+    if partition_size is None or num_partitions is None:
+        if max_context_len is None:
+            max_context_len = int(context_lens.max().item()) if B > 0 else 0
+        if partition_size is None:
+            partition_size, num_partitions = decode_split_plan(B, hkv, max_context_len)
+        else:
+            num_partitions = max(1, -(-max_context_len // partition_size))
+    if out is None:
+        out = torch.empty(B, hq, d, dtype=torch.bfloat16, device=q.device)
+    if num_partitions > 1:
+        if part_out is None:
+            part_out = torch.empty(B, hq, num_partitions, d, dtype=torch.float32, device=q.device)
+        if part_lse is None:
+            part_lse = torch.empty(B, hq, num_partitions, dtype=torch.float32, device=q.device)
+    ptr = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
+    st = load_library().pa_decode_append(
+        ptr(out), ptr(part_out) if num_partitions > 1 else 0,
+        ptr(part_lse) if num_partitions > 1 else 0, q.data_ptr(), k_new.data_ptr(),
+        v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+        context_lens.data_ptr(), B, hq, hkv, d, BLOCK_SIZE, nb, block_tables.shape[1],
+        int(partition_size), int(num_partitions), float(scale), _stream(q.device))
+    _check(st, "pa_decode_append")
+    if num_partitions == 1:
+        return out
     return decode_reduce(part_out, part_lse, context_lens, partition_size, out=out)
 
 

@@ -156,20 +156,61 @@ __device__ __forceinline__ void compute_pair(PairRegs<D>& r, const u32x4 (&qf)[N
     }
 }
 
+// Replaces, in a pair's loaded registers, the key at pair-relative position
+// `rel` (0..31) by the new token's K row pieces `newk` and V values `newv`:
+// the pool may not hold that token yet when the decode kernel appends it
+// itself.  Lane (col, c) holds K rows 8*(gr&1) + (col&3) + 4t (+16 in the
+// second block, gr = col/4) for tiles t = 0, 1, and V^T keys lane_key0..+7
+// of d = 16*dt + col.
+template <int D>
+__device__ __forceinline__ void patch_pair(PairRegs<D>& r, const u32x4 (&newk)[D / 32],
+                                           const uint32_t (&newv)[D / 16], int rel, int col,
+                                           int lane_key0) {
+  const int gr = col >> 2;
+  const int krow = ((gr >= 2) ? kBlock : 0) + 8 * (gr & 1) + (col & 3);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+    if (krow + 4 * t == rel) {
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) r.k[t][i] = newk[i];
+    }
+  const int e = rel - lane_key0;
+  if (e >= 0 && e < 8) {
+    const int w = e >> 1;
+    const uint32_t keep = (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+    const int sh = (e & 1) ? 16 : 0;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (q == w) r.v[dt][q] = (r.v[dt][q] & keep) | (newv[dt] << sh);
+    }
+  }
+}
+
 // Query tokens per sequence: query_len; columns per KV head: query_len *
 // group, taken NT tiles of 16 at a time by `num_chunks` workgroups.  The
 // chunks of one (partition, KV head, sequence) read the same K/V, so they
 // are given launch indices that are equal modulo 8: the hardware deals
 // workgroups to the 8 XCDs round-robin, so they run on one XCD and share
 // its L2.
-template <int D, int NW, int NBUF, int NT>
+//
+// APPEND (one query token per sequence): the kernel also appends the token's
+// K/V (k_new/v_new [B, Hkv, D]) at position ctx-1 through the block table.
+// Every lane holds its slice of the new row from the start; the pair that
+// covers position ctx-1 takes those values instead of the pool's (which may
+// or may not have been written yet), and wave 0 of the workgroup whose
+// partition holds ctx-1 writes the row into the pools.  k_pool/v_pool are
+// the same pools as k_cache/v_cache; no reader depends on those stores.
+template <int D, int NW, int NBUF, int NT, bool APPEND>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(
     uint16_t* __restrict__ out, float* __restrict__ part_out, float* __restrict__ part_lse,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
-    const int32_t* __restrict__ context_lens, int query_len, int num_q_heads, int num_kv_heads,
-    int group, int64_t num_blocks, int max_blocks, int blocks_per_part, int num_partitions,
-    int num_chunks, float scale_log2) {
+    const int32_t* __restrict__ context_lens, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, uint16_t* k_pool, uint16_t* v_pool, int query_len,
+    int num_q_heads, int num_kv_heads, int group, int64_t num_blocks, int max_blocks,
+    int blocks_per_part, int num_partitions, int num_chunks, float scale_log2) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   int item = blockIdx.x, chunk = 0;
@@ -254,6 +295,39 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
   // Lane group c's keys start at block (c >= 2 ? y : x), offset 8*(c&1).
   const int lane_key0 = ((c >= 2) ? kBlock : 0) + 8 * (c & 1);
 
+  // The appended token: this lane's pieces of its K row (the d-slices its
+  // pool K loads cover) and its V values at d = 16*dt + col.
+  const int pos_new = ctx - 1;
+  u32x4 newk[APPEND ? KS : 1];
+  uint32_t newv[APPEND ? DT : 1];
+  if constexpr (APPEND) {
+    const int64_t src = ((int64_t)s * num_kv_heads + g) * D;
+#pragma unroll
+    for (int i = 0; i < KS; ++i) newk[i] = load16(k_new + src + 8 * c + 32 * i);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) newv[dt] = v_new[src + 16 * dt + col];
+    // Wave 0 of the workgroup whose partition holds ctx-1 stores the row
+    // (lanes with col == 0 the K pieces, lanes with c == 0 the V values).
+    if (wave == 0 && chunk == 0 && ctx > 0 && !bad && pos_new / kBlock >= pb0 &&
+        pos_new / kBlock < pb0 + blocks_per_part) {
+      const int64_t blk = bt[pos_new / kBlock];
+      if (blk >= 0 && blk < num_blocks) {
+        const int64_t tile = blk * num_kv_heads + g;
+        const int off = pos_new % kBlock;
+        if (col == 0) {
+          uint16_t* kd = k_pool + (tile * kBlock + off) * D + 8 * c;
+#pragma unroll
+          for (int i = 0; i < KS; ++i) *reinterpret_cast<u32x4*>(kd + 32 * i) = newk[i];
+        }
+        if (c == 0) {
+          uint16_t* vd = v_pool + (tile * D + col) * kBlock + off;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) vd[16 * dt * kBlock] = (uint16_t)newv[dt];
+        }
+      }
+    }
+  }
+
   // Issue the loads of this wave's pair k into `r`.  An entry outside the
   // pool marks the sequence bad (NaN output) and is replaced by block 0 so
   // the loads stay in bounds (num_blocks == 0 never gets here: see above).
@@ -282,6 +356,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
     for (int b = 0; b < NBUF; ++b) {
       const int k = kb + b;
       if (k < nk) {
+        if constexpr (APPEND) {
+          const int rel = pos_new - (wb0 + 2 * k) * kBlock;  // wave-uniform
+          if (rel >= 0 && rel < 2 * kBlock) patch_pair<D>(buf[b], newk, newv, rel, col, lane_key0);
+        }
         compute_pair<D, NT>(buf[b], qf, acc, m_run, l_run, (wb0 + 2 * k) * kBlock + lane_key0,
                             limit, climit, scale_log2);
         if (k + NBUF < nk) issue(k + NBUF, buf[b]);
@@ -469,9 +547,12 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(
 
 int launch_decode(void* out, float* part_out, float* part_lse, const void* q,
                   const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                  const int32_t* context_lens, int num_seqs, int query_len, int num_q_heads,
-                  int num_kv_heads, int head_dim, int64_t num_blocks, int max_blocks_per_seq,
-                  int partition_size, int num_partitions, float scale, hipStream_t stream) {
+                  const int32_t* context_lens, const void* k_new, const void* v_new,
+                  int num_seqs, int query_len, int num_q_heads, int num_kv_heads, int head_dim,
+                  int64_t num_blocks, int max_blocks_per_seq, int partition_size,
+                  int num_partitions, float scale, hipStream_t stream) {
+  const bool append = k_new != nullptr;
+  if (append && query_len != 1) return -2;
   const int group = num_q_heads / num_kv_heads;
   const int tiles = (query_len * group + 15) / 16;
   // Up to two column tiles share a wave's K/V registers; more tiles are
@@ -491,17 +572,21 @@ int launch_decode(void* out, float* part_out, float* part_lse, const void* q,
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(NW * 64), 0, stream, (uint16_t*)out,
                        part_out, part_lse, (const uint16_t*)q, (const uint16_t*)k_cache,
-                       (const uint16_t*)v_cache, block_tables, context_lens, query_len,
-                       num_q_heads, num_kv_heads, group, num_blocks, max_blocks_per_seq, bpp,
-                       num_partitions, chunks, scale_log2);
+                       (const uint16_t*)v_cache, block_tables, context_lens,
+                       (const uint16_t*)k_new, (const uint16_t*)v_new, (uint16_t*)k_cache,
+                       (uint16_t*)v_cache, query_len, num_q_heads, num_kv_heads, group,
+                       num_blocks, max_blocks_per_seq, bpp, num_partitions, chunks, scale_log2);
   };
-  switch (head_dim * 4 + nt) {
-    case 64 * 4 + 1: go(decode_kernel<64, NW, 4, 1>); break;
-    case 64 * 4 + 2: go(decode_kernel<64, NW, 4, 2>); break;
-    case 128 * 4 + 1: go(decode_kernel<128, NW, 1, 1>); break;
-    case 128 * 4 + 2: go(decode_kernel<128, NW, 1, 2>); break;
-    case 256 * 4 + 1: go(decode_kernel<256, NW, 2, 1>); break;
-    case 256 * 4 + 2: go(decode_kernel<256, NW, 1, 2>); break;
+  switch (head_dim * 8 + nt * 2 + (append ? 1 : 0)) {
+    case 64 * 8 + 2: go(decode_kernel<64, NW, 4, 1, false>); break;
+    case 64 * 8 + 4: go(decode_kernel<64, NW, 4, 2, false>); break;
+    case 64 * 8 + 3: go(decode_kernel<64, NW, 4, 1, true>); break;
+    case 128 * 8 + 2: go(decode_kernel<128, NW, 1, 1, false>); break;
+    case 128 * 8 + 4: go(decode_kernel<128, NW, 1, 2, false>); break;
+    case 128 * 8 + 3: go(decode_kernel<128, NW, 1, 1, true>); break;
+    case 256 * 8 + 2: go(decode_kernel<256, NW, 2, 1, false>); break;
+    case 256 * 8 + 4: go(decode_kernel<256, NW, 1, 2, false>); break;
+    case 256 * 8 + 3: go(decode_kernel<256, NW, 2, 1, true>); break;
     default: return -2;
   }
   return hipGetLastError() == hipSuccess ? 0 : -3;

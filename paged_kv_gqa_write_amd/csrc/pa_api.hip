@@ -101,7 +101,34 @@ int pa_decode_multi(void* out, float* part_out, float* part_lse, const void* q,
   if (num_partitions == 1 && !out) return PA_ERR_INVALID_ARG;
   if (num_partitions > 1 && (!part_out || !part_lse)) return PA_ERR_INVALID_ARG;
   return pa::launch_decode(out, part_out, part_lse, q, k_cache, v_cache, block_tables,
-                           context_lens, num_seqs, query_len, num_q_heads, num_kv_heads,
+                           context_lens, nullptr, nullptr, num_seqs, query_len, num_q_heads,
+                           num_kv_heads, head_dim, num_blocks, max_blocks_per_seq,
+                           partition_size, num_partitions, scale, as_stream(stream));
+}
+
+int pa_decode_append(void* out, float* part_out, float* part_lse, const void* q,
+                     const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                     const int32_t* block_tables, const int32_t* context_lens,
+                     int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                     int32_t max_blocks_per_seq, int32_t partition_size,
+                     int32_t num_partitions, float scale, void* stream) {
+  if (num_seqs < 0 || num_blocks < 0) return PA_ERR_INVALID_ARG;
+  int st = check_heads(num_q_heads, num_kv_heads, head_dim, block_size);
+  if (st != PA_OK) return st;
+  if (max_blocks_per_seq <= 0) return PA_ERR_INVALID_ARG;
+  if (partition_size <= 0 || partition_size % kBlockSize != 0) return PA_ERR_INVALID_ARG;
+  if (num_partitions < 1) return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || scale < 0.f) return PA_ERR_INVALID_ARG;
+  if ((int64_t)num_partitions * num_kv_heads * num_seqs > kMaxGrid) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)num_seqs * num_q_heads > kMaxGrid) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !block_tables || !context_lens)
+    return PA_ERR_INVALID_ARG;
+  if (num_partitions == 1 && !out) return PA_ERR_INVALID_ARG;
+  if (num_partitions > 1 && (!part_out || !part_lse)) return PA_ERR_INVALID_ARG;
+  return pa::launch_decode(out, part_out, part_lse, q, k_cache, v_cache, block_tables,
+                           context_lens, k_new, v_new, num_seqs, 1, num_q_heads, num_kv_heads,
                            head_dim, num_blocks, max_blocks_per_seq, partition_size,
                            num_partitions, scale, as_stream(stream));
 }

@@ -13,12 +13,15 @@ int launch_write_kv(const void* k_new, const void* v_new, const int64_t* slot_ma
                     void* k_cache, void* v_cache, int num_tokens, int num_kv_heads,
                     int head_dim, int64_t num_blocks, hipStream_t stream);
 
-// query_len query tokens per sequence (1 for plain decode).
+// query_len query tokens per sequence (1 for plain decode).  With k_new /
+// v_new non-null (query_len 1 only) the kernel also appends each sequence's
+// token at position ctx-1 into the pools through the block table.
 int launch_decode(void* out, float* part_out, float* part_lse, const void* q,
                   const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                  const int32_t* context_lens, int num_seqs, int query_len, int num_q_heads,
-                  int num_kv_heads, int head_dim, int64_t num_blocks, int max_blocks_per_seq,
-                  int partition_size, int num_partitions, float scale, hipStream_t stream);
+                  const int32_t* context_lens, const void* k_new, const void* v_new,
+                  int num_seqs, int query_len, int num_q_heads, int num_kv_heads, int head_dim,
+                  int64_t num_blocks, int max_blocks_per_seq, int partition_size,
+                  int num_partitions, float scale, hipStream_t stream);
 
 int launch_decode_reduce(void* out, const float* part_out, const float* part_lse,
                          const int32_t* context_lens, int num_seqs, int query_len,

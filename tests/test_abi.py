@@ -32,6 +32,7 @@ def lib():
 def test_header_declares_the_boundary():
     assert header_functions() == sorted(["pa_write_kv", "pa_decode", "pa_decode_reduce",
                                          "pa_decode_multi", "pa_decode_multi_reduce",
+                                         "pa_decode_append",
                                          "pa_prefill", "pa_copy_blocks",
                                          "pa_decode_split_plan", "pa_status_string",
                                          "pa_prefix_index_create", "pa_prefix_index_destroy",
@@ -137,6 +138,36 @@ def test_reduce_validation(lib):
     assert _reduce(lib, po=None) == INVALID
     assert _reduce(lib, pl=None) == INVALID
     assert _reduce(lib, B=0, out=None, po=None, pl=None) == OK
+
+
+def _append(lib, **kw):
+    a = dict(out=FAKE, po=FAKE, pl=FAKE, q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, bt=FAKE,
+             ctx=FAKE, B=8, hq=32, hkv=8, d=128, bs=16, nb=4096, mb=72, ps=288, P=4,
+             scale=0.088)
+    a.update(kw)
+    return lib.pa_decode_append(a["out"], a["po"], a["pl"], a["q"], a["kn"], a["vn"], a["kc"],
+                                a["vc"], a["bt"], a["ctx"], a["B"], a["hq"], a["hkv"], a["d"],
+                                a["bs"], a["nb"], a["mb"], a["ps"], a["P"], a["scale"], None)
+
+
+def test_decode_append_validation(lib):
+    assert _append(lib, B=-1) == INVALID
+    assert _append(lib, hq=31) == INVALID
+    assert _append(lib, hq=136, hkv=4) == UNSUPPORTED
+    assert _append(lib, d=72) == UNSUPPORTED
+    assert _append(lib, bs=8) == UNSUPPORTED
+    assert _append(lib, mb=0) == INVALID
+    assert _append(lib, ps=20) == INVALID
+    assert _append(lib, P=0) == INVALID
+    assert _append(lib, scale=float("inf")) == INVALID
+    assert _append(lib, kn=None) == INVALID
+    assert _append(lib, vn=None) == INVALID
+    assert _append(lib, kc=None) == INVALID
+    assert _append(lib, P=1, out=None) == INVALID
+    assert _append(lib, P=4, pl=None) == INVALID
+    assert _append(lib, P=0x40000000) == UNSUPPORTED
+    assert _append(lib, B=0, q=None, kn=None, vn=None, kc=None, vc=None, bt=None, ctx=None,
+                   out=None) == OK
 
 
 def _multi(lib, **kw):

@@ -1,0 +1,98 @@
+"""pa_decode_append (append the new token's K/V and decode, one kernel) on
+the GPU: outputs against the oracle's write_kv + decode, the pools bit-exact
+against the oracle's write_kv, and bit-identical to pa_write_kv + pa_decode.
+The pools are NaN-poisoned at every slot that does not hold a live token --
+the new token's own slot included -- so a kernel that read the new token
+back from the pool instead of its own copy would return NaN."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_gqa_write_amd as pa
+import workloads
+from _gpu_helpers import DEV, announce, check_tolerance, decode_gpu, decode_oracle
+from _helpers import bits
+
+
+def _append_gpu(case, partition_size=None, num_partitions=None):
+    kc, vc = case.k_cache.to(DEV), case.v_cache.to(DEV)
+    out = pa.decode_append(case.q.to(DEV), case.k_new.to(DEV), case.v_new.to(DEV), kc, vc,
+                           case.block_tables.to(DEV), case.context_lens.to(DEV), case.scale,
+                           max_context_len=max(int(case.context_lens.max()), 1),
+                           partition_size=partition_size, num_partitions=num_partitions)
+    torch.cuda.synchronize()
+    return out.cpu(), kc.cpu(), vc.cpu()
+
+
+def _oracle_pools(case):
+    return oracle.write_kv(bits(case.k_cache), bits(case.v_cache), bits(case.k_new),
+                           bits(case.v_new), case.slot_mapping.numpy())
+
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", list(workloads.DECODE_CASES))
+def test_decode_append_config_parity(name):
+    """Every decode workload at full size in the library's split plan."""
+    announce(f"decode_append {name}")
+    case = workloads.DECODE_CASES[name]()
+    out, kc, vc = _append_gpu(case)
+    check_tolerance(name, out, decode_oracle(case), literal=True)
+    ek, ev = _oracle_pools(case)
+    assert np.array_equal(bits(kc), ek) and np.array_equal(bits(vc), ev)
+
+
+@pytest.mark.parametrize("ps", [None, 16, 32, 64, 1152])
+def test_decode_append_equals_write_then_decode_bitwise(ps):
+    announce(f"decode_append vs write_kv+decode ps={ps}")
+    case = workloads.qwen3_4b_decode()
+    out, _, _ = _append_gpu(case, partition_size=ps)
+    assert torch.equal(out, decode_gpu(case, partition_size=ps))
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(4, 2, 64), (32, 8, 128), (16, 2, 256), (16, 1, 128)])
+def test_decode_append_new_token_positions(hq, hkv, d):
+    """The new token at every kind of place: alone (ctx 1), first and last
+    slot of a block, in the first and second block of a 32-key pair, on a
+    partition boundary (ps = 64: ctx-1 = 64 starts partition 1), and a
+    sequence with nothing to append (ctx 0)."""
+    announce(f"decode_append positions hq={hq} hkv={hkv} d={d}")
+    lens = [1, 16, 17, 32, 33, 48, 64, 65, 100, 0, 129]
+    case = workloads.make_decode_case("pos", context_lens=lens, num_q_heads=hq,
+                                      num_kv_heads=hkv, head_dim=d, num_blocks=96,
+                                      seed=hq + d)
+    ref = decode_oracle(case)
+    ek, ev = _oracle_pools(case)
+    for ps, P in [(144, 1), (64, 3), (16, 9)]:
+        out, kc, vc = _append_gpu(case, partition_size=ps, num_partitions=P)
+        check_tolerance(f"positions ps={ps}", out, ref)
+        assert out[9].float().abs().sum().item() == 0
+        assert np.array_equal(bits(kc), ek) and np.array_equal(bits(vc), ev)
+
+
+def test_decode_append_bad_entry_poisons_and_skips_write():
+    """A table entry outside the pool for the new token's block: NaN outputs
+    for that sequence and nothing written for it; the other sequence's token
+    is appended and its output unharmed."""
+    announce("decode_append bad entry")
+    case = workloads.make_decode_case("bad", context_lens=[40, 40], num_q_heads=8,
+                                      num_kv_heads=2, head_dim=128, num_blocks=16, seed=4)
+    ref = decode_oracle(case)
+    ek, ev = oracle.write_kv(bits(case.k_cache), bits(case.v_cache), bits(case.k_new[:1]),
+                             bits(case.v_new[:1]), case.slot_mapping[:1].numpy())
+    case.block_tables[1, 2] = 77             # block of position 39 of sequence 1
+    for ps in (None, 16):
+        out, kc, vc = _append_gpu(case, partition_size=ps)
+        assert torch.isnan(out[1].float()).all()
+        check_tolerance("good sequence", out[:1], ref[:1])
+        assert np.array_equal(bits(kc), ek) and np.array_equal(bits(vc), ev)
+
+
+def test_decode_append_repeat_runs_bitwise_identical():
+    announce("decode_append determinism")
+    case = workloads.qwen3_32b_decode_long()
+    a, _, _ = _append_gpu(case)
+    b, _, _ = _append_gpu(case)
+    assert torch.equal(a, b)

@@ -2,9 +2,10 @@
 Architecture Notes: decode runs as graph replay with pre-allocated buffers).
 
 The library allocates, frees and synchronises nothing and issues no memset,
-so a layer stack of pa_write_kv + pa_decode + pa_decode_reduce launches can
-be captured once and replayed.  Each replay, with eager work and host
-synchronisation in between, must reproduce the eager result bit for bit."""
+so a layer stack of pa_write_kv + pa_decode + pa_decode_reduce launches (or
+pa_decode_append + pa_decode_reduce) can be captured once and replayed.
+Each replay, with eager work and host synchronisation in between, must
+reproduce the eager result bit for bit."""
 import pytest
 import torch
 
@@ -15,8 +16,9 @@ from _gpu_helpers import DEV, announce
 pytestmark = pytest.mark.gpu
 
 
-def test_graph_replayed_decode_step_matches_eager_bitwise():
-    announce("graph-captured decode step")
+@pytest.mark.parametrize("fused", [False, True], ids=["write_then_decode", "decode_append"])
+def test_graph_replayed_decode_step_matches_eager_bitwise(fused):
+    announce(f"graph-captured decode step fused={fused}")
     layers = 3
     case = workloads.qwen3_4b_decode(poison=False)
     B, hq, hkv, d = case.batch, case.num_q_heads, case.num_kv_heads, case.head_dim
@@ -41,9 +43,14 @@ def test_graph_replayed_decode_step_matches_eager_bitwise():
 
     def step():
         for i in range(layers):
-            pa.write_kv(k_new, v_new, slots, kc[i], vc[i])
-            pa.decode(q[i], kc[i], vc[i], bt, ctx, case.scale, partition_size=ps,
-                      num_partitions=P, out=outs[i], part_out=po, part_lse=pl)
+            if fused:
+                pa.decode_append(q[i], k_new, v_new, kc[i], vc[i], bt, ctx, case.scale,
+                                 partition_size=ps, num_partitions=P, out=outs[i], part_out=po,
+                                 part_lse=pl)
+            else:
+                pa.write_kv(k_new, v_new, slots, kc[i], vc[i])
+                pa.decode(q[i], kc[i], vc[i], bt, ctx, case.scale, partition_size=ps,
+                          num_partitions=P, out=outs[i], part_out=po, part_lse=pl)
 
     step()                                   # eager reference
     torch.cuda.synchronize()
