@@ -107,7 +107,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ prefix_lens, int num_seqs, int total_q, int max_q_len,
     int num_q_heads, int num_kv_heads, int group, int64_t num_blocks, int max_blocks,
-    int nslots, float scale_log2) {
+    int nslots, int slot_tokens, float scale_log2) {
   using Cfg = PrefillCfg<D, NT, BK, NW, S>;
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
@@ -129,9 +129,63 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
 
   const int per_slot = num_seqs * num_kv_heads;
   const int bid = blockIdx.x;
-  const int slot = nslots - 1 - bid / per_slot;
-  const int s = (bid % per_slot) / num_kv_heads;
   const int g = bid % num_kv_heads;
+  int slot, s;
+  if (slot_tokens > 0) {
+    // Longest-first order of the (sequence, slot) work items.  The hardware
+    // hands out workgroups in launch order, each to the next free slot of
+    // its XCD, so launching items in decreasing cost keeps the finish times
+    // level (greedy list scheduling).  A slot's cost is its number of key
+    // tiles, ceil((P + min(n, (slot+1)*T)) / BK) with T = slot_tokens tokens
+    // per slot; it grows with the slot, so "how many slots of sequence s
+    // cost at least c" has a closed form.  Lane j handles sequence j
+    // (num_seqs <= 64); every wave finds item number bid / Hkv on its own by
+    // a binary search over the cost threshold.
+    const int ln = threadIdx.x & 63;
+    int ns = 0, pl = 0;
+    if (ln < num_seqs) {
+      const int a = cu_seqlens[ln], b = cu_seqlens[ln + 1];
+      ns = (a >= 0 && b <= total_q && b > a) ? min(b - a, max_q_len) : 0;
+      pl = prefix_lens != nullptr ? max(prefix_lens[ln], 0) : 0;
+    }
+    const int nsl = (ns + slot_tokens - 1) / slot_tokens;
+    auto count = [&](int c) {  // slots of this lane's sequence costing >= c
+      const int x = (c - 1) * BK - pl;
+      return x < 0 ? nsl : (x >= ns ? 0 : nsl - x / slot_tokens);
+    };
+    auto wave_sum = [](int v) {
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+      return v;
+    };
+    const int r = bid / num_kv_heads;
+    if (r >= wave_sum(nsl)) return;
+    int cmax = nsl > 0 ? (pl + ns + BK - 1) / BK : 0;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) cmax = max(cmax, __shfl_xor(cmax, m, 64));
+    int lo = 1, hi = cmax + 1;  // total(lo) > r >= total(hi)
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (wave_sum(count(mid)) > r) lo = mid;
+      else hi = mid;
+    }
+    const int a_lo = count(lo), a_hi = count(lo + 1);
+    const int idx = r - wave_sum(a_hi);
+    int incl = a_lo - a_hi;  // items of cost exactly lo, scanned over lanes
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const int t = __shfl_up(incl, m, 64);
+      if (ln >= m) incl += t;
+    }
+    const int excl = incl - (a_lo - a_hi);
+    const uint64_t hit = __ballot(idx >= excl && idx < incl);
+    if (hit == 0) return;  // unreachable: exactly one lane holds item idx
+    s = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
+    slot = __builtin_amdgcn_readlane(nsl - a_lo + (idx - excl), s);
+  } else {
+    slot = nslots - 1 - bid / per_slot;
+    s = (bid % per_slot) / num_kv_heads;
+  }
 
   const int q0 = cu_seqlens[s];
   const int q1 = cu_seqlens[s + 1];
@@ -557,11 +611,15 @@ int launch_cfg(void* out, const void* q, const void* k_cache, const void* v_cach
   const int64_t nslots = (cols + Cfg::kCols - 1) / Cfg::kCols;
   const int64_t nwg = nslots * num_seqs * num_kv_heads;
   if (nwg > 0x7FFFFFFF) return -2;
+  // Longest-first launch order needs whole tokens per slot and one lane per
+  // sequence; otherwise slots are launched in decreasing slot order.
+  const int slot_tokens =
+      (Cfg::kCols % group == 0 && num_seqs <= 64) ? Cfg::kCols / group : 0;
   hipLaunchKernelGGL((prefill_kernel<D, NT, BK, NW, S, WPE>), dim3((unsigned)nwg), dim3(NW * 64), 0,
                      stream, (uint16_t*)out, (const uint16_t*)q, (const uint16_t*)k_cache,
                      (const uint16_t*)v_cache, block_tables, cu_seqlens, prefix_lens, num_seqs,
                      total_q, max_q_len, num_q_heads, num_kv_heads, group, num_blocks,
-                     max_blocks_per_seq, (int)nslots, scale * kLog2e);
+                     max_blocks_per_seq, (int)nslots, slot_tokens, scale * kLog2e);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
