@@ -100,6 +100,52 @@ __device__ __forceinline__ void wait_lds() {
   __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
 
+// Sum, max and inclusive prefix sum over the 64 lanes of a wave with DPP row
+// operations (a few cycles each, no LDS crossbar).  The values are >= 0, so
+// 0 serves as the identity for lanes a row mask leaves out.  Sum and max
+// leave the total in lane 63.
+__device__ __forceinline__ int dpp(int v, int ctrl, int row_mask) {
+  switch (ctrl) {  // the control is an immediate
+    case 0xB1: return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+    case 0x4E: return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+    case 0x141: return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+    case 0x140: return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);
+    case 0x111: return __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);
+    case 0x112: return __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);
+    case 0x114: return __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);
+    case 0x118: return __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);
+    case 0x142: return __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);
+    default: return __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);
+  }
+}
+__device__ __forceinline__ int wave_total(int v) {
+  v += dpp(v, 0xB1, 0xF);   // quad_perm [1,0,3,2]
+  v += dpp(v, 0x4E, 0xF);   // quad_perm [2,3,0,1]
+  v += dpp(v, 0x141, 0xF);  // row_half_mirror
+  v += dpp(v, 0x140, 0xF);  // row_mirror: every lane holds its row's sum
+  v += dpp(v, 0x142, 0xA);  // row_bcast15 into rows 1 and 3
+  v += dpp(v, 0x143, 0xC);  // row_bcast31 into rows 2 and 3
+  return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ int wave_max_nonneg(int v) {
+  v = max(v, dpp(v, 0xB1, 0xF));
+  v = max(v, dpp(v, 0x4E, 0xF));
+  v = max(v, dpp(v, 0x141, 0xF));
+  v = max(v, dpp(v, 0x140, 0xF));
+  v = max(v, dpp(v, 0x142, 0xA));
+  v = max(v, dpp(v, 0x143, 0xC));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += dpp(v, 0x111, 0xF);  // row_shr:1
+  v += dpp(v, 0x112, 0xF);  // row_shr:2
+  v += dpp(v, 0x114, 0xF);  // row_shr:4
+  v += dpp(v, 0x118, 0xF);  // row_shr:8: scan within each row of 16
+  v += dpp(v, 0x142, 0xA);  // rows 1 and 3 add the previous row's total
+  v += dpp(v, 0x143, 0xC);  // rows 2 and 3 add the total of rows 0-1
+  return v;
+}
+
 template <int D, int NT, int BK, int NW, int S, int WPE>
 __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
@@ -107,7 +153,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ prefix_lens, int num_seqs, int total_q, int max_q_len,
     int num_q_heads, int num_kv_heads, int group, int64_t num_blocks, int max_blocks,
-    int nslots, int slot_tokens, float scale_log2) {
+    int nslots, int slot_shift, float scale_log2) {
   using Cfg = PrefillCfg<D, NT, BK, NW, S>;
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
@@ -130,71 +176,79 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
   const int per_slot = num_seqs * num_kv_heads;
   const int bid = blockIdx.x;
   const int g = bid % num_kv_heads;
-  int slot, s;
-  if (slot_tokens > 0) {
+  int slot, s, q0, q1, P;
+  // Table entries of this wave's block in tiles 0 and 1, fetched with the
+  // sequence lengths when the longest-first order is computed (-1: none).
+  int64_t pre0 = -1, pre1 = -1;
+  bool have_pre = false;
+  if (slot_shift >= 0) {
     // Longest-first order of the (sequence, slot) work items.  The hardware
     // hands out workgroups in launch order, each to the next free slot of
     // its XCD, so launching items in decreasing cost keeps the finish times
     // level (greedy list scheduling).  A slot's cost is its number of key
-    // tiles, ceil((P + min(n, (slot+1)*T)) / BK) with T = slot_tokens tokens
-    // per slot; it grows with the slot, so "how many slots of sequence s
+    // tiles, ceil((P + min(n, (slot+1)*T)) / BK) with T = 2^slot_shift
+    // tokens per slot; it grows with the slot, so "how many slots of sequence s
     // cost at least c" has a closed form.  Lane j handles sequence j
     // (num_seqs <= 64); every wave finds item number bid / Hkv on its own by
     // a binary search over the cost threshold.
     const int ln = threadIdx.x & 63;
-    int ns = 0, pl = 0;
+    int ns = 0, pl = 0, la = 0, lb = 0, lp = 0, le0 = -1, le1 = -1;
+    // This wave's block of a tile (the same formula as below).
+    const int wblk = (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * (Cfg::kDmaK / NW) *
+                      (1024 / (2 * D))) / kBlock;
     if (ln < num_seqs) {
-      const int a = cu_seqlens[ln], b = cu_seqlens[ln + 1];
-      ns = (a >= 0 && b <= total_q && b > a) ? min(b - a, max_q_len) : 0;
-      pl = prefix_lens != nullptr ? max(prefix_lens[ln], 0) : 0;
+      la = cu_seqlens[ln];
+      lb = cu_seqlens[ln + 1];
+      lp = prefix_lens != nullptr ? prefix_lens[ln] : 0;
+      ns = (la >= 0 && lb <= total_q && lb > la) ? min(lb - la, max_q_len) : 0;
+      pl = max(lp, 0);
+      const int32_t* row = block_tables + (int64_t)ln * max_blocks;
+      if (wblk < max_blocks) le0 = row[wblk];
+      if (Cfg::kBlocks + wblk < max_blocks) le1 = row[Cfg::kBlocks + wblk];
     }
-    const int nsl = (ns + slot_tokens - 1) / slot_tokens;
+    const int nsl = (ns + (1 << slot_shift) - 1) >> slot_shift;
     auto count = [&](int c) {  // slots of this lane's sequence costing >= c
       const int x = (c - 1) * BK - pl;
-      return x < 0 ? nsl : (x >= ns ? 0 : nsl - x / slot_tokens);
-    };
-    auto wave_sum = [](int v) {
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-      return v;
+      return x < 0 ? nsl : (x >= ns ? 0 : nsl - (x >> slot_shift));
     };
     const int r = bid / num_kv_heads;
-    if (r >= wave_sum(nsl)) return;
-    int cmax = nsl > 0 ? (pl + ns + BK - 1) / BK : 0;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) cmax = max(cmax, __shfl_xor(cmax, m, 64));
+    if (r >= wave_total(nsl)) return;
+    const int cmax = wave_max_nonneg(nsl > 0 ? (pl + ns + BK - 1) / BK : 0);
     int lo = 1, hi = cmax + 1;  // total(lo) > r >= total(hi)
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (wave_sum(count(mid)) > r) lo = mid;
+      if (wave_total(count(mid)) > r) lo = mid;
       else hi = mid;
     }
     const int a_lo = count(lo), a_hi = count(lo + 1);
-    const int idx = r - wave_sum(a_hi);
-    int incl = a_lo - a_hi;  // items of cost exactly lo, scanned over lanes
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      const int t = __shfl_up(incl, m, 64);
-      if (ln >= m) incl += t;
-    }
+    const int idx = r - wave_total(a_hi);
+    // items of cost exactly lo, scanned over the lanes (sequences)
+    const int incl = wave_inclusive_scan(a_lo - a_hi);
     const int excl = incl - (a_lo - a_hi);
     const uint64_t hit = __ballot(idx >= excl && idx < incl);
     if (hit == 0) return;  // unreachable: exactly one lane holds item idx
     s = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
     slot = __builtin_amdgcn_readlane(nsl - a_lo + (idx - excl), s);
+    // The sequence's bounds and prefix are already in lane s.
+    q0 = __builtin_amdgcn_readlane(la, s);
+    q1 = __builtin_amdgcn_readlane(lb, s);
+    P = __builtin_amdgcn_readlane(lp, s);
+    pre0 = __builtin_amdgcn_readlane(le0, s);
+    pre1 = __builtin_amdgcn_readlane(le1, s);
+    have_pre = true;
   } else {
     slot = nslots - 1 - bid / per_slot;
     s = (bid % per_slot) / num_kv_heads;
+    q0 = cu_seqlens[s];
+    q1 = cu_seqlens[s + 1];
+    P = prefix_lens != nullptr ? prefix_lens[s] : 0;
   }
 
-  const int q0 = cu_seqlens[s];
-  const int q1 = cu_seqlens[s + 1];
   if (q0 < 0 || q1 > total_q || q1 <= q0) return;
   const int nq = min(q1 - q0, max_q_len);
   const int ncols = nq * group;
   const int c0 = slot * Cfg::kCols;
   if (c0 >= ncols) return;
-  const int P = prefix_lens != nullptr ? prefix_lens[s] : 0;
   const int64_t L = (int64_t)P + (q1 - q0);
   const bool bad = P < 0 || (L + kBlock - 1) / kBlock > max_blocks || num_blocks <= 0;
   const int pos_max = (min(ncols, c0 + Cfg::kCols) - 1) / group;
@@ -227,9 +281,9 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
 #pragma unroll
     for (int i = 0; i < KS; ++i) qf[nt][i] = load16(qb + 32 * i);
   }
-  // Q (and nothing else) is in flight: settle it so that from here on the
-  // only vector-memory operations are the tile copies counted below.
-  wait_vm<0>();
+  // Q is left in flight: the first tile's copies are issued behind it, and
+  // the wait before the first tile (vector-memory operations complete in
+  // order) covers both.
 
   // Smallest causal limit over the wave's columns that are written (columns
   // past the sequence take whatever the plain form gives; never stored).
@@ -271,15 +325,23 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
   bool bad_entry = false;
   // Table entry of this wave's block in `tile` (block 0 stands in for blocks
   // past the keys needed -- never weighted -- and for bad entries).
-  auto entry_of = [&](int tile) __attribute__((always_inline)) -> int64_t {
+  auto checked_entry = [&](int tile, auto load) __attribute__((always_inline)) -> int64_t {
     const int lb = tile * Cfg::kBlocks + wave_blk;
     if (tile >= ntiles || lb * kBlock >= kend) return 0;
-    const int64_t p = btc[lb];
+    const int64_t p = load(lb);
     if (p < 0 || p >= num_blocks) {
       bad_entry = true;
       return 0;
     }
     return p;
+  };
+  auto entry_of = [&](int tile) __attribute__((always_inline)) -> int64_t {
+    return checked_entry(tile, [&](int lb) -> int64_t { return btc[lb]; });
+  };
+  // Tiles 0 and 1 from the prefetched entries where there are some.
+  auto first_entry = [&](int tile) __attribute__((always_inline)) -> int64_t {
+    if (!have_pre) return entry_of(tile);
+    return checked_entry(tile, [&](int) -> int64_t { return tile == 0 ? pre0 : pre1; });
   };
   auto issue = [&](int64_t phys, uint8_t* sb) __attribute__((always_inline)) {
     const int64_t tile_base = (phys * num_kv_heads + g) * (int64_t)(kBlock * D);
@@ -501,13 +563,20 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
   // read from the buffers still being filled and inserts no wait of its own.
   // Table entries are fetched one tile ahead of their use.  One pass over all
   // tiles in the given softmax mode; on return no copy is in flight.
-  auto run_pass = [&](auto mode_tag) __attribute__((always_inline)) {
-    if (0 < ntiles) issue(entry_of(0), stage(std::integral_constant<int, 0>{}));
+  auto run_pass = [&](auto mode_tag, bool prefetched) __attribute__((always_inline)) {
+    if (0 < ntiles)
+      issue(prefetched ? first_entry(0) : entry_of(0), stage(std::integral_constant<int, 0>{}));
+    // Two stages: tile 1 goes out at once too (stage 1 is free until then),
+    // so it has the whole of tile 0 to arrive; from tile 1 on, tile t issues
+    // tile t+1.
+    if constexpr (S == 2)
+      if (1 < ntiles)
+        issue(prefetched ? first_entry(1) : entry_of(1), stage(std::integral_constant<int, 1>{}));
     if constexpr (S >= 3)
       if (1 < ntiles) issue(entry_of(1), stage(std::integral_constant<int, 1>{}));
     if constexpr (S >= 4)
       if (2 < ntiles) issue(entry_of(2), stage(std::integral_constant<int, 2>{}));
-    int64_t next_phys = entry_of(S - 1);
+    int64_t next_phys = entry_of(S == 2 ? 2 : S - 1);
     auto step = [&](int t, auto stage_tag, auto first_tag, auto hilo_tag)
         __attribute__((always_inline)) {
       constexpr int ST = decltype(stage_tag)::value;
@@ -520,7 +589,8 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
         if (ahead >= 1) wait_vm<KPW + VPW>();
         else wait_vm<0>();
       } else {
-        wait_vm<0>();
+        if (t == 0 && 1 < ntiles) wait_vm<KPW + VPW>();  // tile 1 may stay in flight
+        else wait_vm<0>();
       }
       // Last tile: zero the V^T values of keys at or past kend in this wave's
       // own copies (complete after the wait above) before publishing them.
@@ -531,7 +601,12 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
       __builtin_amdgcn_s_barrier();
       run_tile(t, stage(std::integral_constant<int, ST>{}), first_tag, mode_tag, hilo_tag,
                [&]() __attribute__((always_inline)) {
-                 if (t + S - 1 < ntiles) {
+                 if constexpr (S == 2) {
+                   if (t >= 1 && t + 1 < ntiles) {
+                     issue(next_phys, stage(std::integral_constant<int, (ST + 1) % 2>{}));
+                     next_phys = entry_of(t + 2);
+                   }
+                 } else if (t + S - 1 < ntiles) {
                    issue(next_phys, stage(std::integral_constant<int, (ST + S - 1) % S>{}));
                    next_phys = entry_of(t + S);
                  }
@@ -554,7 +629,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
     }
   };
 
-  run_pass(std::integral_constant<int, kFixed>{});
+  run_pass(std::integral_constant<int, kFixed>{}, true);
 
   const bool any_bad = __syncthreads_or(bad || bad_entry);
   // The fixed-reference pass is exact unless a score rose more than 2^64
@@ -577,7 +652,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) acc[nt][dt] = f32x4{0, 0, 0, 0};
     }
-    run_pass(std::integral_constant<int, kLazy>{});
+    run_pass(std::integral_constant<int, kLazy>{}, false);
   }
 
   const float nanv = __builtin_nanf("");
@@ -611,15 +686,19 @@ int launch_cfg(void* out, const void* q, const void* k_cache, const void* v_cach
   const int64_t nslots = (cols + Cfg::kCols - 1) / Cfg::kCols;
   const int64_t nwg = nslots * num_seqs * num_kv_heads;
   if (nwg > 0x7FFFFFFF) return -2;
-  // Longest-first launch order needs whole tokens per slot and one lane per
-  // sequence; otherwise slots are launched in decreasing slot order.
-  const int slot_tokens =
-      (Cfg::kCols % group == 0 && num_seqs <= 64) ? Cfg::kCols / group : 0;
+  // Longest-first launch order needs whole tokens per slot (kCols / group,
+  // then a power of two) and one lane per sequence; otherwise slots are
+  // launched in decreasing slot order.
+  int slot_shift = -1;
+  if (Cfg::kCols % group == 0 && num_seqs <= 64) {
+    slot_shift = 0;
+    while ((1 << slot_shift) < Cfg::kCols / group) ++slot_shift;
+  }
   hipLaunchKernelGGL((prefill_kernel<D, NT, BK, NW, S, WPE>), dim3((unsigned)nwg), dim3(NW * 64), 0,
                      stream, (uint16_t*)out, (const uint16_t*)q, (const uint16_t*)k_cache,
                      (const uint16_t*)v_cache, block_tables, cu_seqlens, prefix_lens, num_seqs,
                      total_q, max_q_len, num_q_heads, num_kv_heads, group, num_blocks,
-                     max_blocks_per_seq, (int)nslots, slot_tokens, scale * kLog2e);
+                     max_blocks_per_seq, (int)nslots, slot_shift, scale * kLog2e);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
