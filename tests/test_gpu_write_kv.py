@@ -68,3 +68,34 @@ def test_write_kv_zero_tokens_is_noop():
     pa.write_kv(e, e, torch.empty(0, dtype=torch.int64, device=DEV), kc, vc)
     torch.cuda.synchronize()
     assert kc.abs().sum().item() == 0
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_write_kv_whole_blocks_and_broken_runs(d):
+    """Groups of 16 tokens that fill one block in order take the transposed
+    whole-block store; everything else the per-element one.  Mixed here:
+    whole blocks (including the pool's last block), a block filled in
+    reverse order, a run shifted by one slot, a run with one skipped token,
+    a group spanning two blocks, and a short final group."""
+    announce(f"write_kv whole blocks and broken runs d={d}")
+    g = torch.Generator().manual_seed(300 + d)
+    nb, hkv = 24, 2
+    runs = [torch.arange(16) + 16 * 3,                 # whole block 3
+            torch.arange(16).flip(0) + 16 * 5,         # block 5, reverse order
+            torch.arange(16) + 16 * 7 + 1,             # shifted by one slot (crosses into block 8)
+            torch.cat([torch.arange(7), torch.tensor([-1]), torch.arange(8, 16)]) + 16 * 10,
+            torch.arange(16) + 16 * (nb - 1),          # the pool's last block, whole
+            torch.cat([torch.arange(8) + 16 * 12 + 8, torch.arange(8) + 16 * 13]),
+            torch.arange(16) + 16 * 15,                # whole block 15
+            torch.arange(9) + 16 * 20]                 # short last group
+    slots = torch.cat(runs).to(torch.int64)
+    slots[3 * 16 + 7] = -1 - 16 * 10                   # the -1 inside run 4, kept negative
+    T = slots.numel()
+    k0 = torch.randn(nb, hkv, 16, d, generator=g).to(torch.bfloat16)
+    v0 = torch.randn(nb, hkv, d, 16, generator=g).to(torch.bfloat16)
+    kn = torch.randn(T, hkv, d, generator=g).to(torch.bfloat16)
+    vn = torch.randn(T, hkv, d, generator=g).to(torch.bfloat16)
+    kc, vc = k0.to(DEV), v0.to(DEV)
+    pa.write_kv(kn.to(DEV), vn.to(DEV), slots.to(DEV), kc, vc)
+    torch.cuda.synchronize()
+    _check_pools(kc.cpu(), vc.cpu(), k0, v0, kn, vn, slots)
