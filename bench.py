@@ -314,6 +314,18 @@ def main():
         torch.cuda.synchronize()
         pf_us = t0.elapsed_time(t1) / (args.steps * L) * 1e3
         pf_tflops = flops / (pf_us * 1e-6) / 1e12
+        # pa_write_kv of the 4096 new tokens alone, back to back over the layers
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(args.steps):
+            for i in range(L):
+                lib.pa_write_kv(pkn.data_ptr(), pvn.data_ptr(), pslots.data_ptr(),
+                                pkc[i].data_ptr(), pvc[i].data_ptr(), T, phkv, pd, 16,
+                                pc.num_blocks, sptr)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        wkv_us = t0.elapsed_time(t1) / (args.steps * L) * 1e3
+        wkv_bytes = 2 * 2 * T * phkv * pd * 2     # K and V, read and written
         result["prefill"] = {
             "workload": "qwen3_4b_prefill_4x1024: 4 x 1024 new tokens, sequences 1 and 3 after "
                         "512 cached tokens, 32/8 heads, head_dim 128, 36 layers "
@@ -327,6 +339,14 @@ def main():
                                                      ["prefill.hip", "pa_device.h"]),
                          "kernel": "prefill_kernel<128>", "avg_launch_us": round(pf_us, 3)},
         }
+        result["write_kv"] = {
+            "workload": "pa_write_kv of the 4096 new tokens of qwen3_4b_prefill_4x1024 (8 KV heads, "
+                        "head_dim 128), back to back over 36 layers' pools",
+            "avg_launch_us": round(wkv_us, 3), "bytes_per_launch": wkv_bytes,
+            "roofline": {"bound": "hbm", "achieved": round(wkv_bytes / (wkv_us * 1e-6) / 1e9, 1),
+                         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(wkv_bytes / (wkv_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)},
+            "decode_append_note": "the decode step appends its 8 tokens inside pa_decode_append"}
         del pkc, pvc
         torch.cuda.empty_cache()
 
