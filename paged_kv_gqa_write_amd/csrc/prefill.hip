@@ -714,7 +714,7 @@ int launch_prefill(void* out, const void* q, const void* k_cache, const void* v_
       max_q_len, num_q_heads, num_kv_heads, num_blocks, max_blocks_per_seq, scale, stream
   switch (head_dim) {
     case 64: return launch_cfg<64, 1, 64, 8, 2, 4>(PA_PREFILL_ARGS);
-    case 128: return launch_cfg<128, 1, 32, 8, 2, 4>(PA_PREFILL_ARGS);
+    case 128: return launch_cfg<128, 1, 64, 8, 2, 4>(PA_PREFILL_ARGS);
     case 256: return launch_cfg<256, 1, 32, 8, 2, 1>(PA_PREFILL_ARGS);
     default: return -2;
   }
