@@ -495,14 +495,23 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
       if (HILO) l_acc[nt] = mfma16x16x32(ones, pl[nt], l_acc[nt]);
     }
     const uint8_t* vr = sb + voff + kp * (2 * D * 32);
+    u32x4 a[DT];
+    auto vread = [&](int dt) __attribute__((always_inline)) {
+      a[dt] = *reinterpret_cast<const u32x4*>(vr + dt * (16 * 32));
+    };
+    vread(0);
+    if (DT > 1) vread(1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(vr + dt * (16 * 32));
+      if (dt + 2 < DT) vread(dt + 2);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        acc[nt][dt] = mfma16x16x32(a, pb[nt], acc[nt][dt]);
-        if (HILO) acc[nt][dt] = mfma16x16x32(a, pl[nt], acc[nt][dt]);
+        acc[nt][dt] = mfma16x16x32(a[dt], pb[nt], acc[nt][dt]);
+        if (HILO) acc[nt][dt] = mfma16x16x32(a[dt], pl[nt], acc[nt][dt]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -522,16 +531,24 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
         s0[nt] = f32x4{0, 0, 0, 0};
         s1[nt] = f32x4{0, 0, 0, 0};
       }
+      u32x4 ka[KS], kb[KS];
+      auto kread = [&](int i) __attribute__((always_inline)) {
+        const uint8_t* kr = sb + koff[i] + 32 * kp * (2 * D);
+        ka[i] = *reinterpret_cast<const u32x4*>(kr);
+        kb[i] = *reinterpret_cast<const u32x4*>(kr + 4 * (2 * D));
+      };
+      kread(0);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < KS; ++i) {
-        const uint8_t* kr = sb + koff[i] + 32 * kp * (2 * D);
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(kr);
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(kr + 4 * (2 * D));
+        if (i + 1 < KS) kread(i + 1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          s0[nt] = mfma16x16x32(a0, qf[nt][i], s0[nt]);
-          s1[nt] = mfma16x16x32(a1, qf[nt][i], s1[nt]);
+          s0[nt] = mfma16x16x32(ka[i], qf[nt][i], s0[nt]);
+          s1[nt] = mfma16x16x32(kb[i], qf[nt][i], s1[nt]);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
       if (kp == 0) after_qk();
       // Lane group c holds keys key0 + 0..7 (0..3 from s0, 4..7 from s1).

@@ -109,7 +109,7 @@ def test_prefill_repeat_runs_bitwise_identical():
     assert torch.equal(prefill_gpu(case), prefill_gpu(case))
 
 
-def _weight_rounding_bound(case):
+def _weight_rounding_bound(case, seqs=None):
     """Per-element error bound of attention whose softmax weights enter the
     P.V product as bf16 (fp32 accumulation, normalised by the sum of the same
     rounded weights): with w the exact weights and |delta_j| <= 2^-9 the
@@ -118,14 +118,15 @@ def _weight_rounding_bound(case):
     S = sum_j w_j |v_j - out|.  Returned: 2^-8 S (twice that, covering the
     fp32 score/exp errors, orders of magnitude smaller) plus one bf16 ulp of
     out for the output rounding.  Computed in fp64 from the oracle's own
-    helpers, with the exact output."""
+    helpers, with the exact output.  seqs: only these sequences' rows
+    (others zero)."""
     kc, vc = prefill_oracle_pools(case)
     qf = oracle.bf16_bits_to_f64(bits(case.q))
     out = np.zeros(qf.shape)
     spread = np.zeros(qf.shape)
     bt, cu = case.block_tables.numpy(), case.cu_seqlens.numpy()
     for s, (n, p) in enumerate(zip(case.q_lens, case.prefix_lens_list)):
-        if n == 0:
+        if n == 0 or (seqs is not None and s not in seqs):
             continue
         a = int(cu[s])
         K, V = oracle.gather_sequence(kc, vc, bt[s], p + n)
@@ -212,3 +213,57 @@ def test_prefill_longest_first_order_many_lanes(nseq):
     assert np.isfinite(out).all()
     assert (err <= bound).all(), (err - bound).max()
     assert err.mean() <= 5e-4, err.mean()
+
+
+@pytest.mark.parametrize("nseq,d,maxlen", [(64, 128, 800), (100, 64, 400)],
+                         ids=["longest_first", "slot_order"])
+def test_prefill_many_items_with_reruns_and_a_bad_entry(nseq, d, maxlen):
+    """Thousands of (sequence, column slot, KV head) work items -- about ten
+    per workgroup slot of the GPU, 32 tokens x 4 heads each -- mixing plain
+    items with items that need the re-run pass (keys past position 47 of
+    three sequences scaled by 64, far beyond the fp32 range of the fixed
+    reference), an empty sequence and a sequence whose table entry is out of
+    range (its outputs NaN, nothing else affected).  64 sequences take the
+    longest-first order, 100 the slot order.  Every element against the
+    oracle: the rising sequences held to the bound derived from the weights'
+    rounding, the others to the usual bar."""
+    announce(f"prefill many items nseq={nseq} d={d}")
+    import paged_kv_gqa_write_amd as pa
+    from _gpu_helpers import DEV
+    g = torch.Generator().manual_seed(500 + nseq)
+    q_lens = torch.randint(1, maxlen + 1, (nseq,), generator=g).tolist()
+    prefix_lens = torch.randint(0, 40, (nseq,), generator=g).tolist()
+    q_lens[5] = 0
+    rising, poisoned = [2, 17, nseq - 3], nseq // 2
+    for s in rising:
+        q_lens[s] = 160
+    case = workloads.make_prefill_case("persist", q_lens=q_lens, prefix_lens=prefix_lens,
+                                       num_q_heads=32, num_kv_heads=8, head_dim=d,
+                                       num_blocks=sum((n + p) // 16 + 1
+                                                      for n, p in zip(q_lens, prefix_lens)) + 8,
+                                       seed=600 + nseq)
+    cu = case.cu_seqlens.tolist()
+    for s in rising:
+        rows = torch.arange(cu[s] + 48, cu[s + 1])
+        case.k_new[rows] = (case.k_new[rows].float() * 64.0).to(torch.bfloat16)
+    kc, vc = case.k_cache.to(DEV), case.v_cache.to(DEV)
+    pa.write_kv(case.k_new.to(DEV), case.v_new.to(DEV), case.slot_mapping.to(DEV), kc, vc)
+    bt = case.block_tables.clone()
+    bt[poisoned, 0] = case.num_blocks + 5
+    out = pa.prefill(case.q.to(DEV), kc, vc, bt.to(DEV), case.cu_seqlens.to(DEV),
+                     case.prefix_lens.to(DEV), case.scale, max(q_lens)).cpu()
+    torch.cuda.synchronize()
+    rows_of = lambda ss: np.concatenate([np.arange(cu[s], cu[s + 1]) for s in ss])  # noqa: E731
+    assert torch.isnan(out[rows_of([poisoned])].float()).all()
+    plain = [s for s in range(nseq) if s not in rising and s != poisoned]
+    check_tolerance(f"many items nseq={nseq} plain rows", out[rows_of(plain)],
+                    prefill_oracle(case)[rows_of(plain)], literal=False)
+    ref, bound = _weight_rounding_bound(case, seqs=rising)
+    r = rows_of(rising)
+    o = out[r].float().double().numpy()
+    err = np.abs(o - ref[r])
+    print(f"[bound] many items nseq={nseq} rising rows: max err {err.max():.3g}, "
+          f"max err/bound {(err / bound[r]).max():.3g}", flush=True)
+    assert np.isfinite(o).all()
+    assert (err <= bound[r]).all(), (err - bound[r]).max()
+
