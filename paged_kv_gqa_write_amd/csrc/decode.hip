@@ -4,8 +4,9 @@
 // tokens): every (query token, query head) pair of a KV head is one column.
 //
 // Work decomposition: one workgroup per (partition p, KV head g, sequence s,
-// column chunk), NW waves per workgroup.  The partition's KV blocks are taken two at a time
-// ("pairs", 32 keys); wave w handles a contiguous range of pairs.  All G
+// column chunk), NW waves per workgroup (3 or 4, chosen per shape in the
+// launcher).  The partition's KV blocks are taken two at a time ("pairs", 32
+// keys); wave w handles a contiguous range of pairs.  All G
 // query heads of the KV head are processed together, so each K/V byte is read
 // once.  A wave fetches the block-table entries of up to 32 pairs with one
 // load (lane i holds entry i; pairs read them back with readlane) and keeps
@@ -568,9 +569,14 @@ int launch_decode(void* out, float* part_out, float* part_lse, const void* q,
   if (nwg > 0x7FFFFFFF) return -2;
   const float scale_log2 = scale * kLog2e;
   const int bpp = partition_size / kBlock;
-  constexpr int NW = 4;
-  auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(NW * 64), 0, stream, (uint16_t*)out,
+  // Waves per workgroup and pairs in flight per wave.  head_dim 128 with one
+  // tile: 3 waves, so that with partitions of 9 pairs (the batch-8 plan)
+  // every wave takes exactly 3 pairs.  The plain form keeps 2 pairs in flight
+  // per wave (Qwen3-4B batch 8: 11.4 -> 10.1 us against 4 waves with 1 pair
+  // in flight); the appending form keeps 1 (11.2 -> 10.8 us; with 2 its
+  // register patching makes the compiler wait for both pairs).
+  auto go = [&](auto kern, int nw) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(nw * 64), 0, stream, (uint16_t*)out,
                        part_out, part_lse, (const uint16_t*)q, (const uint16_t*)k_cache,
                        (const uint16_t*)v_cache, block_tables, context_lens,
                        (const uint16_t*)k_new, (const uint16_t*)v_new, (uint16_t*)k_cache,
@@ -578,15 +584,15 @@ int launch_decode(void* out, float* part_out, float* part_lse, const void* q,
                        num_blocks, max_blocks_per_seq, bpp, num_partitions, chunks, scale_log2);
   };
   switch (head_dim * 8 + nt * 2 + (append ? 1 : 0)) {
-    case 64 * 8 + 2: go(decode_kernel<64, NW, 4, 1, false>); break;
-    case 64 * 8 + 4: go(decode_kernel<64, NW, 4, 2, false>); break;
-    case 64 * 8 + 3: go(decode_kernel<64, NW, 4, 1, true>); break;
-    case 128 * 8 + 2: go(decode_kernel<128, NW, 1, 1, false>); break;
-    case 128 * 8 + 4: go(decode_kernel<128, NW, 1, 2, false>); break;
-    case 128 * 8 + 3: go(decode_kernel<128, NW, 1, 1, true>); break;
-    case 256 * 8 + 2: go(decode_kernel<256, NW, 2, 1, false>); break;
-    case 256 * 8 + 4: go(decode_kernel<256, NW, 1, 2, false>); break;
-    case 256 * 8 + 3: go(decode_kernel<256, NW, 2, 1, true>); break;
+    case 64 * 8 + 2: go(decode_kernel<64, 4, 4, 1, false>, 4); break;
+    case 64 * 8 + 4: go(decode_kernel<64, 4, 4, 2, false>, 4); break;
+    case 64 * 8 + 3: go(decode_kernel<64, 4, 4, 1, true>, 4); break;
+    case 128 * 8 + 2: go(decode_kernel<128, 3, 2, 1, false>, 3); break;
+    case 128 * 8 + 4: go(decode_kernel<128, 4, 1, 2, false>, 4); break;
+    case 128 * 8 + 3: go(decode_kernel<128, 3, 1, 1, true>, 3); break;
+    case 256 * 8 + 2: go(decode_kernel<256, 4, 2, 1, false>, 4); break;
+    case 256 * 8 + 4: go(decode_kernel<256, 4, 1, 2, false>, 4); break;
+    case 256 * 8 + 3: go(decode_kernel<256, 4, 2, 1, true>, 4); break;
     default: return -2;
   }
   return hipGetLastError() == hipSuccess ? 0 : -3;

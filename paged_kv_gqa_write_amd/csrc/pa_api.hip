@@ -224,9 +224,10 @@ int pa_decode_split_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t max_con
   if (!partition_size || !num_partitions) return PA_ERR_INVALID_ARG;
   if (num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0 || num_compute_units <= 0)
     return PA_ERR_INVALID_ARG;
-  // The decode kernel runs one 4-wave workgroup per compute unit, so aim for
+  // The decode kernel is latency-bound when a launch is small, so aim for
   // one workgroup per CU: split each (sequence, KV head) into enough
-  // partitions, but never below 4 pairs of blocks (one 32-key pair per wave).
+  // partitions, but never below 4 pairs of blocks (at least one 32-key pair
+  // per wave of a 3- or 4-wave workgroup).
   // Partitions are whole pairs (multiples of 32 tokens); the waves of a
   // workgroup split a partition's pairs evenly.
   constexpr int64_t kPair = 32;
