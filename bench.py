@@ -389,7 +389,7 @@ def verify_leg(args, lib, dev, gen, stream, L):
     q = case.q.to(dev)
     k_new, v_new, slots = case.k_new.to(dev), case.v_new.to(dev), case.slot_mapping.to(dev)
     bt, ctx = case.block_tables.to(dev), case.context_lens.to(dev)
-    ps, npart = pa.decode_split_plan(B, hkv, int(case.context_lens.max()))
+    ps, npart = pa.decode_multi_split_plan(B, T, hq, hkv, int(case.context_lens.max()))
     out = torch.empty(B, T, hq, d, dtype=torch.bfloat16, device=dev)
     part_out = torch.empty(B, T, hq, npart, d, dtype=torch.float32, device=dev)
     part_lse = torch.empty(B, T, hq, npart, dtype=torch.float32, device=dev)

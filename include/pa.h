@@ -304,6 +304,23 @@ int pa_decode_split_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t max_con
                          int32_t* partition_size, int32_t* num_partitions);
 
 /*
+ * pa_decode_multi_split_plan -- host-only helper: partition size and count
+ * for pa_decode_multi with T = query_len tokens per sequence.  Its columns
+ * (token, query head) come in 16-wide tiles that may be spread over several
+ * workgroups, so the plan counts workgroups the way pa_decode_multi launches
+ * them and takes the most partitions (whole 32-key pairs, at least 128 keys
+ * each) whose launch holds at most one workgroup per compute unit
+ * (pa_decode_split_plan may round up to slightly more).  num_q_heads must be
+ * a multiple of num_kv_heads.  Writes *partition_size (multiple of 16) and
+ * *num_partitions, covering max_context_len; returns PA_OK or
+ * PA_ERR_INVALID_ARG.
+ */
+int pa_decode_multi_split_plan(int32_t num_seqs, int32_t query_len, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t max_context_len,
+                               int32_t num_compute_units,
+                               int32_t* partition_size, int32_t* num_partitions);
+
+/*
  * Prefix-block index (host only, no GPU involved): which physical KV blocks
  * already hold the leading full blocks of a token sequence ("Qwen3-4B / 8B /
  * 32B", Architecture Notes: prefix caching on by default, prefix matching

@@ -51,6 +51,8 @@ _SIGNATURES = {
     "pa_copy_blocks": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _vp, _i64, _vp, _i32, _i32, _i32,
                                       _i32, _vp]),
     "pa_decode_split_plan": (ctypes.c_int, [_i32, _i32, _i32, _i32, _pi32, _pi32]),
+    "pa_decode_multi_split_plan": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, _pi32,
+                                                  _pi32]),
     "pa_prefix_index_create": (ctypes.c_int, [_i64, _pvp]),
     "pa_prefix_index_destroy": (None, [_vp]),
     "pa_prefix_index_size": (ctypes.c_int64, [_vp]),
@@ -154,6 +156,19 @@ def decode_split_plan(num_seqs: int, num_kv_heads: int, max_context_len: int,
                                              int(max_context_len), int(num_compute_units),
                                              ctypes.byref(ps), ctypes.byref(npart))
     _check(st, "pa_decode_split_plan")
+    return ps.value, npart.value
+
+
+def decode_multi_split_plan(num_seqs: int, query_len: int, num_q_heads: int, num_kv_heads: int,
+                            max_context_len: int, num_compute_units: int | None = None):
+    """(partition_size, num_partitions) for decode_multi from the library's host heuristic."""
+    if num_compute_units is None:
+        num_compute_units = torch.cuda.get_device_properties(0).multi_processor_count
+    ps, npart = ctypes.c_int32(0), ctypes.c_int32(0)
+    st = load_library().pa_decode_multi_split_plan(
+        int(num_seqs), int(query_len), int(num_q_heads), int(num_kv_heads), int(max_context_len),
+        int(num_compute_units), ctypes.byref(ps), ctypes.byref(npart))
+    _check(st, "pa_decode_multi_split_plan")
     return ps.value, npart.value
 
 
@@ -374,8 +389,8 @@ def decode_multi(q, k_cache, v_cache, block_tables, context_lens, scale, *,
         if max_context_len is None:
             max_context_len = int(context_lens.max().item()) if B > 0 else 0
         if partition_size is None:
-            partition_size, num_partitions = decode_split_plan(B, k_cache.shape[1],
-                                                               max_context_len)
+            partition_size, num_partitions = decode_multi_split_plan(
+                B, T, hq, k_cache.shape[1], max_context_len)
         else:
             num_partitions = max(1, -(-max_context_len // partition_size))
     if num_partitions == 1:

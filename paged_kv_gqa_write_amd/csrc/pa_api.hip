@@ -2,6 +2,7 @@
 // then a launch on the caller's stream.  Nothing here allocates, frees or
 // synchronises.  Every check happens before any HIP call, so an invalid call
 // returns without touching the device.
+#include <algorithm>
 #include <math.h>
 #include <stdint.h>
 
@@ -245,6 +246,54 @@ int pa_decode_split_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t max_con
   if (ps > 0x7FFFFFF0LL) return PA_ERR_INVALID_ARG;
   *partition_size = (int32_t)ps;
   *num_partitions = (int32_t)np;
+  return PA_OK;
+}
+
+int pa_decode_multi_split_plan(int32_t num_seqs, int32_t query_len, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t max_context_len,
+                               int32_t num_compute_units, int32_t* partition_size,
+                               int32_t* num_partitions) {
+  if (!partition_size || !num_partitions) return PA_ERR_INVALID_ARG;
+  if (num_seqs < 0 || query_len < 1 || num_kv_heads <= 0 || num_q_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0 || max_context_len < 0 || num_compute_units <= 0)
+    return PA_ERR_INVALID_ARG;
+  // Workgroups of a launch with P partitions, as pa_decode_multi makes them:
+  // items = P x KV heads x sequences; T*G columns in tiles of 16; two tiles
+  // per wave once items x ceil(tiles/2) fill the CUs, else one tile per
+  // workgroup (a workgroup per tile).  The plan takes the most partitions
+  // whose launch still fits in one workgroup per CU (more than that adds a
+  // second dispatch round), in whole 32-key pairs and at least 4 pairs each.
+  constexpr int64_t kPair = 32;
+  constexpr int64_t kMinPart = 4 * kPair;
+  const int64_t tiles = ((int64_t)query_len * (num_q_heads / num_kv_heads) + 15) / 16;
+  const int64_t base = (int64_t)num_seqs * num_kv_heads;
+  const int64_t cus = num_compute_units;
+  const int64_t ctx = max_context_len > 0 ? max_context_len : 1;
+  auto shape = [&](int64_t parts, int64_t& ps, int64_t& np) {
+    ps = (ctx + parts - 1) / parts;
+    ps = ((ps + kPair - 1) / kPair) * kPair;
+    np = (ctx + ps - 1) / ps;
+    if (np == 1) ps = ((ctx + kBlockSize - 1) / kBlockSize) * kBlockSize;
+  };
+  auto workgroups = [&](int64_t np) {
+    const int64_t items = base * np;
+    const bool two = tiles >= 2 && items * ((tiles + 1) / 2) >= cus;
+    return items * (two ? (tiles + 1) / 2 : tiles);
+  };
+  int64_t best_ps = 0, best_np = 0;
+  shape(1, best_ps, best_np);
+  const int64_t max_parts = std::min<int64_t>((ctx + kMinPart - 1) / kMinPart, cus);
+  for (int64_t parts = 2; parts <= max_parts && base > 0; ++parts) {
+    int64_t ps, np;
+    shape(parts, ps, np);
+    if (np > best_np && workgroups(np) <= cus) {
+      best_ps = ps;
+      best_np = np;
+    }
+  }
+  if (best_ps > 0x7FFFFFF0LL) return PA_ERR_INVALID_ARG;
+  *partition_size = (int32_t)best_ps;
+  *num_partitions = (int32_t)best_np;
   return PA_OK;
 }
 

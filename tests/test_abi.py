@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
                                          "pa_decode_multi", "pa_decode_multi_reduce",
                                          "pa_decode_append",
                                          "pa_prefill", "pa_copy_blocks",
-                                         "pa_decode_split_plan", "pa_status_string",
+                                         "pa_decode_split_plan", "pa_decode_multi_split_plan",
+                                         "pa_status_string",
                                          "pa_prefix_index_create", "pa_prefix_index_destroy",
                                          "pa_prefix_index_size", "pa_prefix_index_match",
                                          "pa_prefix_index_insert", "pa_prefix_index_remove"])
@@ -308,3 +309,56 @@ def test_split_plan_validation(lib):
     assert lib.pa_decode_split_plan(-1, 1, 10, 256, ctypes.byref(ps), ctypes.byref(npart)) == INVALID
     assert lib.pa_decode_split_plan(1, 0, 10, 256, ctypes.byref(ps), ctypes.byref(npart)) == INVALID
     assert lib.pa_decode_split_plan(1, 1, 10, 0, ctypes.byref(ps), ctypes.byref(npart)) == INVALID
+
+
+def mplan(lib, B, T, hq, hkv, ctx, cus=256):
+    ps, npart = ctypes.c_int32(), ctypes.c_int32()
+    st = lib.pa_decode_multi_split_plan(B, T, hq, hkv, ctx, cus, ctypes.byref(ps),
+                                        ctypes.byref(npart))
+    return st, ps.value, npart.value
+
+
+def _launch_workgroups(B, T, hq, hkv, npart, cus=256):
+    """Workgroups pa_decode_multi launches (its tile rule, restated)."""
+    tiles = -(-(T * (hq // hkv)) // 16)
+    items = B * hkv * npart
+    two = tiles >= 2 and items * ((tiles + 1) // 2) >= cus
+    return items * (((tiles + 1) // 2) if two else tiles)
+
+
+def test_multi_split_plan_measured_shapes(lib):
+    # Qwen3-4B verify, T = 8, longest context 1110: the partition sizes that
+    # were fastest in a sweep of forced sizes on MI355X (batch 1: 128;
+    # batch 4: 288, one tile per workgroup in two column chunks; batch 8:
+    # 288, two tiles per wave).
+    assert mplan(lib, 1, 8, 32, 8, 1110) == (OK, 128, 9)
+    assert mplan(lib, 4, 8, 32, 8, 1110) == (OK, 288, 4)
+    assert mplan(lib, 8, 8, 32, 8, 1110) == (OK, 288, 4)
+    # one token per sequence: the batch-8 decode plan
+    assert mplan(lib, 8, 1, 32, 8, 1110) == (OK, 288, 4)
+
+
+@pytest.mark.parametrize("B,T,hq,hkv,ctx", [(1, 8, 32, 8, 1110), (4, 8, 32, 8, 1110),
+                                            (8, 8, 32, 8, 1110), (8, 8, 16, 2, 8192),
+                                            (2, 3, 4, 2, 50), (1, 16, 16, 1, 1), (1, 1, 8, 8, 0),
+                                            (64, 2, 64, 8, 1152), (3, 5, 12, 4, 3000)])
+def test_multi_split_plan_covers_context_within_the_cus(lib, B, T, hq, hkv, ctx):
+    st, ps, npart = mplan(lib, B, T, hq, hkv, ctx)
+    assert st == OK
+    assert ps > 0 and ps % 16 == 0 and npart >= 1
+    assert ps * npart >= max(ctx, 1)
+    if npart > 1:
+        assert ps % 32 == 0 and ps >= 128
+        assert ps * (npart - 1) < ctx
+        assert _launch_workgroups(B, T, hq, hkv, npart) <= 256
+
+
+def test_multi_split_plan_validation(lib):
+    ps, npart = ctypes.c_int32(), ctypes.c_int32()
+    f = lib.pa_decode_multi_split_plan
+    assert f(1, 1, 8, 8, 10, 256, None, ctypes.byref(npart)) == INVALID
+    assert f(1, 0, 8, 8, 10, 256, ctypes.byref(ps), ctypes.byref(npart)) == INVALID
+    assert f(1, 1, 6, 4, 10, 256, ctypes.byref(ps), ctypes.byref(npart)) == INVALID
+    assert f(-1, 1, 8, 8, 10, 256, ctypes.byref(ps), ctypes.byref(npart)) == INVALID
+    assert f(1, 1, 8, 8, -1, 256, ctypes.byref(ps), ctypes.byref(npart)) == INVALID
+    assert f(1, 1, 8, 8, 10, 0, ctypes.byref(ps), ctypes.byref(npart)) == INVALID
