@@ -569,9 +569,9 @@ int launch_decode(void* out, float* part_out, float* part_lse, const void* q,
   if (nwg > 0x7FFFFFFF) return -2;
   const float scale_log2 = scale * kLog2e;
   const int bpp = partition_size / kBlock;
-  // Waves per workgroup and pairs in flight per wave.  head_dim 128 with one
-  // tile: 3 waves, so that with partitions of 9 pairs (the batch-8 plan)
-  // every wave takes exactly 3 pairs.  The plain form keeps 2 pairs in flight
+  // Waves per workgroup and pairs in flight per wave.  head_dim 128: 3 waves,
+  // so that with partitions of 9 pairs (the batch-8 plans) every wave takes
+  // exactly 3 pairs (two-tile form, Qwen3-4B verify batch 8: 13.8 -> 13.1 us).  The plain form keeps 2 pairs in flight
   // per wave (Qwen3-4B batch 8: 11.4 -> 10.1 us against 4 waves with 1 pair
   // in flight); the appending form keeps 1 (11.2 -> 10.8 us; with 2 its
   // register patching makes the compiler wait for both pairs).
@@ -588,7 +588,7 @@ int launch_decode(void* out, float* part_out, float* part_lse, const void* q,
     case 64 * 8 + 4: go(decode_kernel<64, 4, 4, 2, false>, 4); break;
     case 64 * 8 + 3: go(decode_kernel<64, 4, 4, 1, true>, 4); break;
     case 128 * 8 + 2: go(decode_kernel<128, 3, 2, 1, false>, 3); break;
-    case 128 * 8 + 4: go(decode_kernel<128, 4, 1, 2, false>, 4); break;
+    case 128 * 8 + 4: go(decode_kernel<128, 3, 1, 2, false>, 3); break;
     case 128 * 8 + 3: go(decode_kernel<128, 3, 1, 1, true>, 3); break;
     case 256 * 8 + 2: go(decode_kernel<256, 4, 2, 1, false>, 4); break;
     case 256 * 8 + 4: go(decode_kernel<256, 4, 1, 2, false>, 4); break;
