@@ -571,7 +571,8 @@ int launch_decode(void* out, float* part_out, float* part_lse, const void* q,
   const int bpp = partition_size / kBlock;
   // Waves per workgroup and pairs in flight per wave.  head_dim 128: 3 waves,
   // so that with partitions of 9 pairs (the batch-8 plans) every wave takes
-  // exactly 3 pairs (two-tile form, Qwen3-4B verify batch 8: 13.8 -> 13.1 us).  The plain form keeps 2 pairs in flight
+  // exactly 3 pairs (two-tile form, Qwen3-4B verify batch 8: 13.8 -> 13.1 us,
+  // 12.8 with 2 pairs in flight).  The plain form keeps 2 pairs in flight
   // per wave (Qwen3-4B batch 8: 11.4 -> 10.1 us against 4 waves with 1 pair
   // in flight); the appending form keeps 1 (11.2 -> 10.8 us; with 2 its
   // register patching makes the compiler wait for both pairs).
@@ -588,7 +589,7 @@ int launch_decode(void* out, float* part_out, float* part_lse, const void* q,
     case 64 * 8 + 4: go(decode_kernel<64, 4, 4, 2, false>, 4); break;
     case 64 * 8 + 3: go(decode_kernel<64, 4, 4, 1, true>, 4); break;
     case 128 * 8 + 2: go(decode_kernel<128, 3, 2, 1, false>, 3); break;
-    case 128 * 8 + 4: go(decode_kernel<128, 3, 1, 2, false>, 3); break;
+    case 128 * 8 + 4: go(decode_kernel<128, 3, 2, 2, false>, 3); break;
     case 128 * 8 + 3: go(decode_kernel<128, 3, 1, 1, true>, 3); break;
     case 256 * 8 + 2: go(decode_kernel<256, 4, 2, 1, false>, 4); break;
     case 256 * 8 + 4: go(decode_kernel<256, 4, 1, 2, false>, 4); break;
