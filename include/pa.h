@@ -52,7 +52,10 @@
  *     the size arguments: a block-table entry outside [0, num_blocks) that a
  *     live position needs, a length that exceeds max_blocks_per_seq*16, or a
  *     decode context longer than partition_size*num_partitions makes the
- *     affected sequence's outputs NaN (and its split-K LSEs NaN).
+ *     affected sequence's outputs NaN (and its split-K LSEs NaN).  So does a
+ *     negative context length, in every call that reads one (the reduces
+ *     included).  The product num_partitions*partition_size must stay below
+ *     2^31 - 64 (PA_ERR_UNSUPPORTED otherwise).
  *   Supported shapes: head_dim in {64, 128, 256}; num_q_heads a multiple of
  *     num_kv_heads with a group Hq/Hkv of at most 16; block_size == 16.
  *   Sizes of 0 (no tokens, no sequences) are valid no-ops.
@@ -166,7 +169,8 @@ int pa_decode_append(void* out, float* part_out, float* part_lse,
  * zero when every partition is empty; NaN when any read LSE is NaN.
  *
  *   context_lens   device int32 [num_seqs] or NULL.  When given, only the
- *                  partitions p < ceil(ctx/partition_size) are read; when
+ *                  partitions p < ceil(ctx/partition_size) are read (none
+ *                  for ctx == 0: zero output; ctx < 0 is invalid: NaN); when
  *                  NULL all num_partitions are read (empty ones must hold
  *                  lse = -inf, as pa_decode writes them).
  *   other arguments as for pa_decode.
@@ -302,6 +306,24 @@ int pa_copy_blocks(void* dst_k_cache, void* dst_v_cache, int64_t dst_num_blocks,
 int pa_decode_split_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
                          int32_t num_compute_units,
                          int32_t* partition_size, int32_t* num_partitions);
+
+/*
+ * pa_decode_split_plan_lens -- host-only helper: the same plan from the
+ * batch's actual context lengths (context_lens: HOST int32 [num_seqs], may
+ * be NULL when num_seqs == 0).  pa_decode launches one workgroup per
+ * (partition, KV head, sequence); those whose partition starts past their
+ * sequence's length exit at once.  The plan takes the smallest partition
+ * (whole 32-key pairs, at least 128 keys) whose live workgroups number at
+ * most num_compute_units, so that in a batch of mixed lengths the long
+ * sequences get more partitions; when one partition per sequence already
+ * gives at least num_compute_units live workgroups, one partition of the
+ * longest context (rounded up to 16).  Writes *partition_size (multiple of
+ * 16) and *num_partitions, covering the longest context; returns PA_OK or
+ * PA_ERR_INVALID_ARG.
+ */
+int pa_decode_split_plan_lens(int32_t num_seqs, int32_t num_kv_heads,
+                              const int32_t* context_lens, int32_t num_compute_units,
+                              int32_t* partition_size, int32_t* num_partitions);
 
 /*
  * pa_decode_multi_split_plan -- host-only helper: partition size and count

@@ -19,7 +19,8 @@ import torch
 __all__ = [
     "PAError", "load_library", "library_path", "write_kv", "decode", "decode_partials",
     "decode_reduce", "decode_append", "decode_multi", "decode_multi_partials", "decode_multi_reduce", "prefill",
-    "copy_blocks", "PrefixIndex", "decode_split_plan", "status_string", "EXPORTED_SYMBOLS",
+    "copy_blocks", "PrefixIndex", "decode_split_plan", "decode_split_plan_lens",
+    "decode_multi_split_plan", "status_string", "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -51,6 +52,7 @@ _SIGNATURES = {
     "pa_copy_blocks": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _vp, _i64, _vp, _i32, _i32, _i32,
                                       _i32, _vp]),
     "pa_decode_split_plan": (ctypes.c_int, [_i32, _i32, _i32, _i32, _pi32, _pi32]),
+    "pa_decode_split_plan_lens": (ctypes.c_int, [_i32, _i32, _vp, _i32, _pi32, _pi32]),
     "pa_decode_multi_split_plan": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, _pi32,
                                                   _pi32]),
     "pa_prefix_index_create": (ctypes.c_int, [_i64, _pvp]),
@@ -108,6 +110,8 @@ def _stream(device: torch.device) -> int:
 
 
 def _need(t: torch.Tensor, name: str, dtype, ndim: int | None = None):
+    """Type, dtype, rank and contiguity of an argument.  Where it lives is
+    checked separately (_on_gpu), after every shape check of the call."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
@@ -116,8 +120,34 @@ def _need(t: torch.Tensor, name: str, dtype, ndim: int | None = None):
         raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _need_shape(t, name: str, dtype, shape):
+    """A caller-supplied output or workspace (None: not given) must have
+    exactly the shape the kernels write: a larger one would be only partly
+    written, a smaller one overrun."""
+    if t is None:
+        return
+    _need(t, name, dtype, len(shape))
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(int(x) for x in shape)}, "
+                         f"got {tuple(t.shape)}")
+
+
+def _on_gpu(*tensors):
+    """Every given tensor (None skipped) is GPU memory of one device; returns
+    that device."""
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("every tensor argument must be a GPU tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"tensors on different devices: {dev} and {t.device}")
+    return dev
 
 
 def _pools(k_cache, v_cache):
@@ -140,6 +170,7 @@ def write_kv(k_new, v_new, slot_mapping, k_cache, v_cache):
     if tuple(k_new.shape) != (T, hkv, d) or tuple(v_new.shape) != (T, hkv, d) \
             or slot_mapping.shape[0] != T:
         raise ValueError("k_new/v_new must be [T, Hkv, D] and slot_mapping [T]")
+    _on_gpu(k_new, v_new, slot_mapping, k_cache, v_cache)
     st = load_library().pa_write_kv(k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(),
                                     k_cache.data_ptr(), v_cache.data_ptr(), T, hkv, d,
                                     BLOCK_SIZE, nb, _stream(k_cache.device))
@@ -159,6 +190,28 @@ def decode_split_plan(num_seqs: int, num_kv_heads: int, max_context_len: int,
     return ps.value, npart.value
 
 
+def decode_split_plan_lens(num_kv_heads: int, context_lens,
+                           num_compute_units: int | None = None):
+    """(partition_size, num_partitions) from the batch's actual context
+    lengths (a host sequence of ints): long sequences of a mixed batch get
+    more partitions (pa_decode_split_plan_lens)."""
+    import numpy as np
+    if isinstance(context_lens, torch.Tensor):
+        if context_lens.is_cuda:
+            raise ValueError("context_lens for the host plan must be host memory")
+        context_lens = context_lens.numpy()
+    lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int64).astype(np.int32))
+    if num_compute_units is None:
+        num_compute_units = torch.cuda.get_device_properties(0).multi_processor_count
+    ps, npart = ctypes.c_int32(0), ctypes.c_int32(0)
+    st = load_library().pa_decode_split_plan_lens(int(lens.size), int(num_kv_heads),
+                                                  lens.ctypes.data if lens.size else None,
+                                                  int(num_compute_units), ctypes.byref(ps),
+                                                  ctypes.byref(npart))
+    _check(st, "pa_decode_split_plan_lens")
+    return ps.value, npart.value
+
+
 def decode_multi_split_plan(num_seqs: int, query_len: int, num_q_heads: int, num_kv_heads: int,
                             max_context_len: int, num_compute_units: int | None = None):
     """(partition_size, num_partitions) for decode_multi from the library's host heuristic."""
@@ -172,50 +225,128 @@ def decode_multi_split_plan(num_seqs: int, query_len: int, num_q_heads: int, num
     return ps.value, npart.value
 
 
-def _decode_call(out, part_out, part_lse, q, k_cache, v_cache, block_tables, context_lens,
-                 scale, partition_size, num_partitions):
+def _plan(B, T, hq, hkv, context_lens, max_context_len, partition_size, num_partitions):
+    """The split-K plan of a decode call: the library's heuristic unless the
+    caller gives a partition size (then enough partitions to cover the
+    longest context)."""
+    if partition_size is not None and num_partitions is not None:
+        return int(partition_size), int(num_partitions)
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if B > 0 else 0
+    if partition_size is None:
+        if T == 1:
+            return decode_split_plan(B, hkv, max_context_len)
+        return decode_multi_split_plan(B, T, hq, hkv, max_context_len)
+    return int(partition_size), max(1, -(-max_context_len // int(partition_size)))
+
+
+def _decode_checks(q, k_cache, v_cache, block_tables, context_lens, T, out, part_out, part_lse,
+                   num_partitions, k_new=None, v_new=None):
+    """Shapes of a decode call's inputs and of the buffers it writes; returns
+    (B, Hq, Hkv, D, num_blocks).  T = 0: q is [B, Hq, D] (one query token);
+    otherwise q is [B, T, Hq, D]."""
     nb, hkv, d = _pools(k_cache, v_cache)
-    _need(q, "q", torch.bfloat16, 3)
+    _need(q, "q", torch.bfloat16, 3 if T == 0 else 4)
     _need(block_tables, "block_tables", torch.int32, 2)
     _need(context_lens, "context_lens", torch.int32, 1)
-    B, hq, dq = q.shape
+    if T == 0:
+        B, hq, dq = q.shape
+        lead = (B,)
+    else:
+        B, Tq, hq, dq = q.shape
+        if Tq != T:
+            raise ValueError(f"q must be [B, {T}, Hq, D], got {tuple(q.shape)}")
+        lead = (B, T)
     if dq != d or block_tables.shape[0] != B or context_lens.shape[0] != B:
-        raise ValueError("q [B, Hq, D], block_tables [B, max_blocks], context_lens [B] mismatch")
-    ptr = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
-    st = load_library().pa_decode(ptr(out), ptr(part_out), ptr(part_lse), q.data_ptr(),
-                                  k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
-                                  context_lens.data_ptr(), B, hq, hkv, d, BLOCK_SIZE, nb,
-                                  block_tables.shape[1], int(partition_size),
-                                  int(num_partitions), float(scale), _stream(q.device))
+        raise ValueError("q [B, (T,) Hq, D], block_tables [B, max_blocks], context_lens [B] "
+                         "mismatch")
+    if hq % hkv != 0:
+        raise ValueError(f"num_q_heads {hq} is not a multiple of num_kv_heads {hkv}")
+    if k_new is not None:
+        _need_shape(k_new, "k_new", torch.bfloat16, (B, hkv, d))
+        _need_shape(v_new, "v_new", torch.bfloat16, (B, hkv, d))
+    P = int(num_partitions)
+    if P < 1:
+        raise ValueError("num_partitions must be >= 1")
+    if P == 1:
+        if out is None:
+            raise ValueError("out is required with one partition")
+        _need_shape(out, "out", torch.bfloat16, (*lead, hq, d))
+    else:
+        if part_out is None or part_lse is None:
+            raise ValueError("part_out and part_lse are required with more than one partition")
+        _need_shape(part_out, "part_out", torch.float32, (*lead, hq, P, d))
+        _need_shape(part_lse, "part_lse", torch.float32, (*lead, hq, P))
+        _need_shape(out, "out", torch.bfloat16, (*lead, hq, d))
+    _on_gpu(q, k_cache, v_cache, block_tables, context_lens, k_new, v_new, out, part_out,
+            part_lse)
+    return B, hq, hkv, d, nb
+
+
+def _ptr(t):
+    return 0 if t is None else t.data_ptr()
+
+
+def _decode_call(out, part_out, part_lse, q, k_cache, v_cache, block_tables, context_lens,
+                 scale, partition_size, num_partitions):
+    B, hq, hkv, d, nb = _decode_checks(q, k_cache, v_cache, block_tables, context_lens, 0, out,
+                                       part_out, part_lse, num_partitions)
+    P = int(num_partitions)
+    st = load_library().pa_decode(_ptr(out) if P == 1 else 0, _ptr(part_out), _ptr(part_lse),
+                                  q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                  block_tables.data_ptr(), context_lens.data_ptr(), B, hq, hkv, d,
+                                  BLOCK_SIZE, nb, block_tables.shape[1], int(partition_size), P,
+                                  float(scale), _stream(q.device))
     _check(st, "pa_decode")
+
+
+def _workspace(q, lead, hq, P, d, part_out, part_lse):
+    if part_out is None:
+        part_out = torch.empty(*lead, hq, P, d, dtype=torch.float32, device=q.device)
+    if part_lse is None:
+        part_lse = torch.empty(*lead, hq, P, dtype=torch.float32, device=q.device)
+    return part_out, part_lse
 
 
 def decode_partials(q, k_cache, v_cache, block_tables, context_lens, scale, partition_size,
                     num_partitions, part_out=None, part_lse=None):
     """Split-K pieces only (num_partitions > 1): (part_out [B,Hq,P,D], part_lse [B,Hq,P])."""
+    if int(num_partitions) < 2:
+        raise ValueError("decode_partials needs num_partitions > 1")
+    _need(q, "q", torch.bfloat16, 3)
     B, hq, d = q.shape
-    if part_out is None:
-        part_out = torch.empty(B, hq, num_partitions, d, dtype=torch.float32, device=q.device)
-    if part_lse is None:
-        part_lse = torch.empty(B, hq, num_partitions, dtype=torch.float32, device=q.device)
+    part_out, part_lse = _workspace(q, (B,), hq, int(num_partitions), d, part_out, part_lse)
     _decode_call(None, part_out, part_lse, q, k_cache, v_cache, block_tables, context_lens,
                  scale, partition_size, num_partitions)
     return part_out, part_lse
 
 
+def _reduce_checks(part_out, part_lse, context_lens, out, T):
+    _need(part_out, "part_out", torch.float32, 4 if T == 0 else 5)
+    if T == 0:
+        B, hq, P, d = part_out.shape
+        lead = (B,)
+    else:
+        B, Tq, hq, P, d = part_out.shape
+        lead = (B, Tq)
+    if part_lse is None:
+        raise ValueError("part_lse is required")
+    _need_shape(part_lse, "part_lse", torch.float32, (*lead, hq, P))
+    if context_lens is not None:
+        _need_shape(context_lens, "context_lens", torch.int32, (B,))
+    _need_shape(out, "out", torch.bfloat16, (*lead, hq, d))
+    _on_gpu(part_out, part_lse, context_lens, out)
+    return lead, hq, P, d
+
+
 def decode_reduce(part_out, part_lse, context_lens, partition_size, out=None):
     """Log-sum-exp combine of split-K pieces into bf16 [B, Hq, D]."""
-    _need(part_out, "part_out", torch.float32, 4)
-    _need(part_lse, "part_lse", torch.float32, 3)
-    B, hq, P, d = part_out.shape
-    if context_lens is not None:
-        _need(context_lens, "context_lens", torch.int32, 1)
+    lead, hq, P, d = _reduce_checks(part_out, part_lse, context_lens, out, 0)
     if out is None:
-        out = torch.empty(B, hq, d, dtype=torch.bfloat16, device=part_out.device)
+        out = torch.empty(*lead, hq, d, dtype=torch.bfloat16, device=part_out.device)
     st = load_library().pa_decode_reduce(out.data_ptr(), part_out.data_ptr(), part_lse.data_ptr(),
-                                         0 if context_lens is None else context_lens.data_ptr(),
-                                         B, hq, d, int(partition_size), P,
-                                         _stream(part_out.device))
+                                         _ptr(context_lens), lead[0], hq, d,
+                                         int(partition_size), P, _stream(part_out.device))
     _check(st, "pa_decode_reduce")
     return out
 
@@ -225,25 +356,22 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, *, max_contex
     """Decode attention, one query token per sequence -> bf16 [B, Hq, D].
 
     The split-K plan comes from the library heuristic unless given; with more
-    than one partition the pieces are combined by pa_decode_reduce."""
+    than one partition the pieces are combined by pa_decode_reduce.  Given
+    out / part_out / part_lse must have exactly the shapes written."""
+    _need(q, "q", torch.bfloat16, 3)
     B, hq, d = q.shape
+    ps, P = _plan(B, 1, hq, k_cache.shape[1], context_lens, max_context_len, partition_size,
+                  num_partitions)
+    _need_shape(out, "out", torch.bfloat16, (B, hq, d))
     if out is None:
         out = torch.empty(B, hq, d, dtype=torch.bfloat16, device=q.device)
-    if partition_size is None:
-        if max_context_len is None:
-            max_context_len = int(context_lens.max().item()) if B > 0 else 0
-        partition_size, num_partitions = decode_split_plan(B, k_cache.shape[1], max_context_len)
-    elif num_partitions is None:
-        if max_context_len is None:
-            max_context_len = int(context_lens.max().item()) if B > 0 else 0
-        num_partitions = max(1, -(-max_context_len // partition_size))
-    if num_partitions == 1:
+    if P == 1:
         _decode_call(out, None, None, q, k_cache, v_cache, block_tables, context_lens, scale,
-                     partition_size, 1)
+                     ps, 1)
         return out
     part_out, part_lse = decode_partials(q, k_cache, v_cache, block_tables, context_lens, scale,
-                                         partition_size, num_partitions, part_out, part_lse)
-    return decode_reduce(part_out, part_lse, context_lens, partition_size, out=out)
+                                         ps, P, part_out, part_lse)
+    return decode_reduce(part_out, part_lse, context_lens, ps, out=out)
 
 
 def decode_append(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, *,
@@ -252,42 +380,28 @@ def decode_append(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
     """Append each sequence's new token (k_new/v_new [B, Hkv, D], position
     ctx-1, slot from the block table) and decode, in one kernel; with more
     than one partition the pieces are combined by pa_decode_reduce."""
-    nb, hkv, d = _pools(k_cache, v_cache)
     _need(q, "q", torch.bfloat16, 3)
-    _need(k_new, "k_new", torch.bfloat16, 3)
-    _need(v_new, "v_new", torch.bfloat16, 3)
-    _need(block_tables, "block_tables", torch.int32, 2)
-    _need(context_lens, "context_lens", torch.int32, 1)
-    B, hq, dq = q.shape
-    if dq != d or block_tables.shape[0] != B or context_lens.shape[0] != B \
-            or tuple(k_new.shape) != (B, hkv, d) or tuple(v_new.shape) != (B, hkv, d):
-        raise ValueError("q [B, Hq, D], k_new/v_new [B, Hkv, D], block_tables [B, max_blocks], "
-                         "context_lens [B] mismatch")
-    if partition_size is None or num_partitions is None:
-        if max_context_len is None:
-            max_context_len = int(context_lens.max().item()) if B > 0 else 0
-        if partition_size is None:
-            partition_size, num_partitions = decode_split_plan(B, hkv, max_context_len)
-        else:
-            num_partitions = max(1, -(-max_context_len // partition_size))
+    B, hq, d = q.shape
+    ps, P = _plan(B, 1, hq, k_cache.shape[1], context_lens, max_context_len, partition_size,
+                  num_partitions)
+    _need_shape(out, "out", torch.bfloat16, (B, hq, d))
     if out is None:
         out = torch.empty(B, hq, d, dtype=torch.bfloat16, device=q.device)
-    if num_partitions > 1:
-        if part_out is None:
-            part_out = torch.empty(B, hq, num_partitions, d, dtype=torch.float32, device=q.device)
-        if part_lse is None:
-            part_lse = torch.empty(B, hq, num_partitions, dtype=torch.float32, device=q.device)
-    ptr = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
+    if P > 1:
+        part_out, part_lse = _workspace(q, (B,), hq, P, d, part_out, part_lse)
+    else:
+        part_out = part_lse = None
+    B, hq, hkv, d, nb = _decode_checks(q, k_cache, v_cache, block_tables, context_lens, 0, out,
+                                       part_out, part_lse, P, k_new, v_new)
     st = load_library().pa_decode_append(
-        ptr(out), ptr(part_out) if num_partitions > 1 else 0,
-        ptr(part_lse) if num_partitions > 1 else 0, q.data_ptr(), k_new.data_ptr(),
+        _ptr(out), _ptr(part_out), _ptr(part_lse), q.data_ptr(), k_new.data_ptr(),
         v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
-        context_lens.data_ptr(), B, hq, hkv, d, BLOCK_SIZE, nb, block_tables.shape[1],
-        int(partition_size), int(num_partitions), float(scale), _stream(q.device))
+        context_lens.data_ptr(), B, hq, hkv, d, BLOCK_SIZE, nb, block_tables.shape[1], ps, P,
+        float(scale), _stream(q.device))
     _check(st, "pa_decode_append")
-    if num_partitions == 1:
+    if P == 1:
         return out
-    return decode_reduce(part_out, part_lse, context_lens, partition_size, out=out)
+    return decode_reduce(part_out, part_lse, context_lens, ps, out=out)
 
 
 def prefill(q, k_cache, v_cache, block_tables, cu_seqlens, prefix_lens, scale, max_q_len,
@@ -301,18 +415,19 @@ def prefill(q, k_cache, v_cache, block_tables, cu_seqlens, prefix_lens, scale, m
     _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
     S = cu_seqlens.shape[0] - 1
     if prefix_lens is not None:
-        _need(prefix_lens, "prefix_lens", torch.int32, 1)
-        if prefix_lens.shape[0] != S:
-            raise ValueError("prefix_lens must be [num_seqs]")
+        _need_shape(prefix_lens, "prefix_lens", torch.int32, (S,))
     total_q, hq, dq = q.shape
     if dq != d or block_tables.shape[0] != S:
         raise ValueError("q [total_q, Hq, D] / block_tables [S, max_blocks] mismatch")
+    if hq % hkv != 0:
+        raise ValueError(f"num_q_heads {hq} is not a multiple of num_kv_heads {hkv}")
+    _need_shape(out, "out", torch.bfloat16, (total_q, hq, d))
+    _on_gpu(q, k_cache, v_cache, block_tables, cu_seqlens, prefix_lens, out)
     if out is None:
         out = torch.empty_like(q)
     st = load_library().pa_prefill(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(),
                                    v_cache.data_ptr(), block_tables.data_ptr(),
-                                   cu_seqlens.data_ptr(),
-                                   0 if prefix_lens is None else prefix_lens.data_ptr(),
+                                   cu_seqlens.data_ptr(), _ptr(prefix_lens),
                                    S, total_q, int(max_q_len), hq, hkv, d, BLOCK_SIZE, nb,
                                    block_tables.shape[1], float(scale), _stream(q.device))
     _check(st, "pa_prefill")
@@ -325,21 +440,17 @@ def prefill(q, k_cache, v_cache, block_tables, cu_seqlens, prefix_lens, scale, m
 
 def _decode_multi_call(out, part_out, part_lse, q, k_cache, v_cache, block_tables, context_lens,
                        scale, partition_size, num_partitions):
-    nb, hkv, d = _pools(k_cache, v_cache)
     _need(q, "q", torch.bfloat16, 4)
-    _need(block_tables, "block_tables", torch.int32, 2)
-    _need(context_lens, "context_lens", torch.int32, 1)
-    B, T, hq, dq = q.shape
-    if dq != d or block_tables.shape[0] != B or context_lens.shape[0] != B:
-        raise ValueError("q [B, T, Hq, D], block_tables [B, max_blocks], context_lens [B] "
-                         "mismatch")
-    ptr = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
-    st = load_library().pa_decode_multi(ptr(out), ptr(part_out), ptr(part_lse), q.data_ptr(),
-                                        k_cache.data_ptr(), v_cache.data_ptr(),
-                                        block_tables.data_ptr(), context_lens.data_ptr(), B, T,
-                                        hq, hkv, d, BLOCK_SIZE, nb, block_tables.shape[1],
-                                        int(partition_size), int(num_partitions), float(scale),
-                                        _stream(q.device))
+    T = q.shape[1]
+    B, hq, hkv, d, nb = _decode_checks(q, k_cache, v_cache, block_tables, context_lens, T, out,
+                                       part_out, part_lse, num_partitions)
+    P = int(num_partitions)
+    st = load_library().pa_decode_multi(_ptr(out) if P == 1 else 0, _ptr(part_out),
+                                        _ptr(part_lse), q.data_ptr(), k_cache.data_ptr(),
+                                        v_cache.data_ptr(), block_tables.data_ptr(),
+                                        context_lens.data_ptr(), B, T, hq, hkv, d, BLOCK_SIZE, nb,
+                                        block_tables.shape[1], int(partition_size), P,
+                                        float(scale), _stream(q.device))
     _check(st, "pa_decode_multi")
 
 
@@ -347,11 +458,11 @@ def decode_multi_partials(q, k_cache, v_cache, block_tables, context_lens, scale
                           partition_size, num_partitions, part_out=None, part_lse=None):
     """Split-K pieces of a multi-token decode (num_partitions > 1):
     (part_out [B, T, Hq, P, D], part_lse [B, T, Hq, P])."""
+    if int(num_partitions) < 2:
+        raise ValueError("decode_multi_partials needs num_partitions > 1")
+    _need(q, "q", torch.bfloat16, 4)
     B, T, hq, d = q.shape
-    if part_out is None:
-        part_out = torch.empty(B, T, hq, num_partitions, d, dtype=torch.float32, device=q.device)
-    if part_lse is None:
-        part_lse = torch.empty(B, T, hq, num_partitions, dtype=torch.float32, device=q.device)
+    part_out, part_lse = _workspace(q, (B, T), hq, int(num_partitions), d, part_out, part_lse)
     _decode_multi_call(None, part_out, part_lse, q, k_cache, v_cache, block_tables,
                        context_lens, scale, partition_size, num_partitions)
     return part_out, part_lse
@@ -359,17 +470,13 @@ def decode_multi_partials(q, k_cache, v_cache, block_tables, context_lens, scale
 
 def decode_multi_reduce(part_out, part_lse, context_lens, partition_size, out=None):
     """Log-sum-exp combine of multi-token split-K pieces into bf16 [B, T, Hq, D]."""
-    _need(part_out, "part_out", torch.float32, 5)
-    _need(part_lse, "part_lse", torch.float32, 4)
-    B, T, hq, P, d = part_out.shape
-    if context_lens is not None:
-        _need(context_lens, "context_lens", torch.int32, 1)
+    lead, hq, P, d = _reduce_checks(part_out, part_lse, context_lens, out, 1)
+    B, T = lead
     if out is None:
         out = torch.empty(B, T, hq, d, dtype=torch.bfloat16, device=part_out.device)
     st = load_library().pa_decode_multi_reduce(
-        out.data_ptr(), part_out.data_ptr(), part_lse.data_ptr(),
-        0 if context_lens is None else context_lens.data_ptr(), B, T, hq, d,
-        int(partition_size), P, _stream(part_out.device))
+        out.data_ptr(), part_out.data_ptr(), part_lse.data_ptr(), _ptr(context_lens), B, T, hq,
+        d, int(partition_size), P, _stream(part_out.device))
     _check(st, "pa_decode_multi_reduce")
     return out
 
@@ -382,25 +489,20 @@ def decode_multi(q, k_cache, v_cache, block_tables, context_lens, scale, *,
     context_lens counts every cached token including the T query tokens
     (whose K/V are already in the pool); token t sits at position
     ctx - T + t and sees keys 0..ctx - T + t."""
+    _need(q, "q", torch.bfloat16, 4)
     B, T, hq, d = q.shape
+    ps, P = _plan(B, T, hq, k_cache.shape[1], context_lens, max_context_len, partition_size,
+                  num_partitions)
+    _need_shape(out, "out", torch.bfloat16, (B, T, hq, d))
     if out is None:
         out = torch.empty(B, T, hq, d, dtype=torch.bfloat16, device=q.device)
-    if partition_size is None or num_partitions is None:
-        if max_context_len is None:
-            max_context_len = int(context_lens.max().item()) if B > 0 else 0
-        if partition_size is None:
-            partition_size, num_partitions = decode_multi_split_plan(
-                B, T, hq, k_cache.shape[1], max_context_len)
-        else:
-            num_partitions = max(1, -(-max_context_len // partition_size))
-    if num_partitions == 1:
+    if P == 1:
         _decode_multi_call(out, None, None, q, k_cache, v_cache, block_tables, context_lens,
-                           scale, partition_size, 1)
+                           scale, ps, 1)
         return out
     part_out, part_lse = decode_multi_partials(q, k_cache, v_cache, block_tables, context_lens,
-                                               scale, partition_size, num_partitions, part_out,
-                                               part_lse)
-    return decode_multi_reduce(part_out, part_lse, context_lens, partition_size, out=out)
+                                               scale, ps, P, part_out, part_lse)
+    return decode_multi_reduce(part_out, part_lse, context_lens, ps, out=out)
 
 
 # ---------------------------------------------------------------------------

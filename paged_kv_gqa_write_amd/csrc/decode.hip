@@ -492,7 +492,9 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(
     np = ctx <= 0 ? 0 : (int)min((int64_t)num_partitions,
                                  ((int64_t)ctx + partition_size - 1) / partition_size);
   float M = -INFINITY;
-  bool nan_seen = false;
+  // A negative length is invalid device data: NaN, as the decode kernel
+  // itself gives such a sequence when it writes the output directly.
+  bool nan_seen = context_lens != nullptr && ctx < 0;
   for (int p0 = 0; p0 < np; p0 += 64) {
     const float v = (p0 + lane < np) ? (p0 == 0 ? lse0 : lse[p0 + lane]) : -INFINITY;
     nan_seen |= v != v;

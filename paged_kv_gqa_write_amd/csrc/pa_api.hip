@@ -27,6 +27,13 @@ int check_heads(int32_t hq, int32_t hkv, int32_t d, int32_t bs) {
   return PA_OK;
 }
 
+// The kernels index positions and blocks inside the partitions' cover
+// (num_partitions * partition_size tokens, plus up to one 32-key pair past
+// its end) with 32-bit integers.
+bool covers_in_int32(int32_t partition_size, int32_t num_partitions) {
+  return (int64_t)partition_size * num_partitions <= 0x7FFFFFFFLL - 64;
+}
+
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 // The address under which the kernels may access a caller's buffer: device
@@ -90,6 +97,7 @@ int pa_decode_multi(void* out, float* part_out, float* part_lse, const void* q,
   if (max_blocks_per_seq <= 0) return PA_ERR_INVALID_ARG;
   if (partition_size <= 0 || partition_size % kBlockSize != 0) return PA_ERR_INVALID_ARG;
   if (num_partitions < 1) return PA_ERR_INVALID_ARG;
+  if (!covers_in_int32(partition_size, num_partitions)) return PA_ERR_UNSUPPORTED;
   if (!isfinite(scale) || scale < 0.f) return PA_ERR_INVALID_ARG;
   // Launch size (one workgroup per 32 columns of a partition) and the
   // number of output rows both index with 32-bit integers.
@@ -120,6 +128,7 @@ int pa_decode_append(void* out, float* part_out, float* part_lse, const void* q,
   if (max_blocks_per_seq <= 0) return PA_ERR_INVALID_ARG;
   if (partition_size <= 0 || partition_size % kBlockSize != 0) return PA_ERR_INVALID_ARG;
   if (num_partitions < 1) return PA_ERR_INVALID_ARG;
+  if (!covers_in_int32(partition_size, num_partitions)) return PA_ERR_UNSUPPORTED;
   if (!isfinite(scale) || scale < 0.f) return PA_ERR_INVALID_ARG;
   if ((int64_t)num_partitions * num_kv_heads * num_seqs > kMaxGrid) return PA_ERR_UNSUPPORTED;
   if ((int64_t)num_seqs * num_q_heads > kMaxGrid) return PA_ERR_UNSUPPORTED;
@@ -155,6 +164,7 @@ int pa_decode_multi_reduce(void* out, const float* part_out, const float* part_l
   if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
   if (partition_size <= 0 || partition_size % kBlockSize != 0) return PA_ERR_INVALID_ARG;
   if (num_partitions < 1) return PA_ERR_INVALID_ARG;
+  if (!covers_in_int32(partition_size, num_partitions)) return PA_ERR_UNSUPPORTED;
   if ((int64_t)query_len * num_q_heads > kMaxGrid) return PA_ERR_UNSUPPORTED;
   if ((int64_t)num_seqs * query_len * num_q_heads > kMaxGrid) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
@@ -243,6 +253,54 @@ int pa_decode_split_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t max_con
   ps = ((ps + kPair - 1) / kPair) * kPair;
   int64_t np = (ctx + ps - 1) / ps;
   if (np == 1) ps = ((ctx + kBlockSize - 1) / kBlockSize) * kBlockSize;
+  if (ps > 0x7FFFFFF0LL) return PA_ERR_INVALID_ARG;
+  *partition_size = (int32_t)ps;
+  *num_partitions = (int32_t)np;
+  return PA_OK;
+}
+
+int pa_decode_split_plan_lens(int32_t num_seqs, int32_t num_kv_heads,
+                              const int32_t* context_lens, int32_t num_compute_units,
+                              int32_t* partition_size, int32_t* num_partitions) {
+  if (!partition_size || !num_partitions) return PA_ERR_INVALID_ARG;
+  if (num_seqs < 0 || num_kv_heads <= 0 || num_compute_units <= 0) return PA_ERR_INVALID_ARG;
+  if (num_seqs > 0 && !context_lens) return PA_ERR_INVALID_ARG;
+  // A launch holds one workgroup per (partition, KV head, sequence); the
+  // ones whose partition lies past their sequence's length exit at once.
+  // The longest workgroup sets the launch time, so take the smallest
+  // partition (whole 32-key pairs, at least 4 of them) whose live
+  // workgroups still fit one per compute unit, counted over the actual
+  // lengths: a batch mixing short and long contexts then gives its long
+  // sequences more partitions instead of leaving compute units idle.
+  constexpr int64_t kPair = 32;
+  constexpr int64_t kMinPart = 4 * kPair;
+  int64_t max_ctx = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) max_ctx = std::max<int64_t>(max_ctx, context_lens[s]);
+  const int64_t ctx = max_ctx > 0 ? max_ctx : 1;
+  auto live = [&](int64_t ps) {
+    int64_t n = 0;
+    for (int32_t s = 0; s < num_seqs; ++s)
+      if (context_lens[s] > 0) n += ((int64_t)context_lens[s] + ps - 1) / ps;
+    return n * num_kv_heads;
+  };
+  const int64_t whole = ((ctx + kBlockSize - 1) / kBlockSize) * kBlockSize;
+  int64_t ps = whole, np = 1;
+  const int64_t k_hi = (ctx + kPair - 1) / kPair;  // ps = 32*k_hi covers ctx in one piece
+  if (k_hi > kMinPart / kPair && live(kPair * k_hi) < num_compute_units) {
+    // One piece per sequence leaves compute units idle.  live() does not
+    // increase with ps: find the smallest k >= 4 with live(32k) <= CUs
+    // (k_hi satisfies it).
+    int64_t lo = kMinPart / kPair, hi = k_hi;  // invariant: live(32*hi) <= CUs
+    if (live(kPair * lo) <= num_compute_units) hi = lo;
+    while (hi - lo > 1) {  // invariant: live(32*lo) > CUs
+      const int64_t mid = (lo + hi) / 2;
+      if (live(kPair * mid) <= num_compute_units) hi = mid;
+      else lo = mid;
+    }
+    ps = kPair * hi;
+    np = (ctx + ps - 1) / ps;
+    if (np == 1) ps = whole;
+  }
   if (ps > 0x7FFFFFF0LL) return PA_ERR_INVALID_ARG;
   *partition_size = (int32_t)ps;
   *num_partitions = (int32_t)np;

@@ -85,3 +85,51 @@ def bf16_tolerance_report(gpu_f64: np.ndarray, ref_f64: np.ndarray, atol=4e-3):
         "n_nonfinite": int(np.count_nonzero(~np.isfinite(gpu_f64))),
         "n": int(err.size),
     }
+
+
+def relayout(case, mapping, num_blocks=None):
+    """The same case with its pool blocks moved: physical block `old` becomes
+    `mapping[old]` for every block the table references (a dict old -> new;
+    a full permutation moves every block).  Pools, block table and slot
+    mapping are rewritten to match; blocks no one maps to hold bf16 NaN.
+    Works for decode, multi-token and prefill cases (any dataclass with
+    k_cache, v_cache, block_tables and slot_mapping)."""
+    import dataclasses
+    nb = num_blocks or case.k_cache.shape[0]
+    olds = torch.tensor(sorted(mapping), dtype=torch.long)
+    news = torch.tensor([mapping[int(o)] for o in olds], dtype=torch.long)
+    nan = torch.tensor(int(NAN_BITS), dtype=torch.int32).to(torch.int16)
+    k2 = torch.empty((nb,) + tuple(case.k_cache.shape[1:]), dtype=torch.int16).fill_(nan)
+    v2 = torch.empty((nb,) + tuple(case.v_cache.shape[1:]), dtype=torch.int16).fill_(nan)
+    k2[news] = case.k_cache.view(torch.int16)[olds]
+    v2[news] = case.v_cache.view(torch.int16)[olds]
+    lut = torch.full((case.k_cache.shape[0],), -1, dtype=torch.long)
+    lut[olds] = news
+    bt = case.block_tables.long()
+    bt2 = torch.where(bt >= 0, lut[bt.clamp(min=0)], bt).to(torch.int32)
+    sl = case.slot_mapping
+    sl2 = torch.where(sl >= 0, lut[(sl // BLOCK).clamp(min=0)] * BLOCK + sl % BLOCK, sl)
+    kw = dict(k_cache=k2.view(torch.bfloat16), v_cache=v2.view(torch.bfloat16),
+              block_tables=bt2, slot_mapping=sl2)
+    if hasattr(case, "num_blocks"):
+        kw["num_blocks"] = nb
+    return dataclasses.replace(case, **kw)
+
+
+def permuted_case(case, seed=1):
+    """Every physical block moved by a seeded random permutation of the pool."""
+    nb = case.k_cache.shape[0]
+    perm = torch.randperm(nb, generator=torch.Generator().manual_seed(seed))
+    return relayout(case, {b: int(perm[b]) for b in range(nb)})
+
+
+def contiguous_twin(case):
+    """The case with each sequence's blocks laid out one after another from
+    block 0, in logical order (identity-like table), other blocks NaN."""
+    mapping, nxt = {}, 0
+    for row in case.block_tables.tolist():
+        for b in row:
+            if b >= 0 and b not in mapping:
+                mapping[b] = nxt
+                nxt += 1
+    return relayout(case, mapping)

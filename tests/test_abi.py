@@ -35,6 +35,7 @@ def test_header_declares_the_boundary():
                                          "pa_decode_append",
                                          "pa_prefill", "pa_copy_blocks",
                                          "pa_decode_split_plan", "pa_decode_multi_split_plan",
+                                         "pa_decode_split_plan_lens",
                                          "pa_status_string",
                                          "pa_prefix_index_create", "pa_prefix_index_destroy",
                                          "pa_prefix_index_size", "pa_prefix_index_match",
@@ -362,3 +363,72 @@ def test_multi_split_plan_validation(lib):
     assert f(-1, 1, 8, 8, 10, 256, ctypes.byref(ps), ctypes.byref(npart)) == INVALID
     assert f(1, 1, 8, 8, -1, 256, ctypes.byref(ps), ctypes.byref(npart)) == INVALID
     assert f(1, 1, 8, 8, 10, 0, ctypes.byref(ps), ctypes.byref(npart)) == INVALID
+
+
+def test_partition_cover_must_fit_int32(lib):
+    # num_partitions * partition_size indexes positions with 32-bit integers
+    # in the kernels: a cover of 2^36 tokens passes every other check.
+    big = dict(ps=1 << 24, P=4096)
+    assert _decode(lib, **big) == UNSUPPORTED
+    assert _append(lib, **big) == UNSUPPORTED
+    assert _multi(lib, **big) == UNSUPPORTED
+    assert _reduce(lib, **big) == UNSUPPORTED
+    assert _multi_reduce(lib, **big) == UNSUPPORTED
+    assert _decode(lib, ps=1 << 26, P=32) == UNSUPPORTED      # exactly 2^31
+
+
+def lplan(lib, hkv, lens, cus=256):
+    arr = (ctypes.c_int32 * max(len(lens), 1))(*lens)
+    ps, npart = ctypes.c_int32(), ctypes.c_int32()
+    st = lib.pa_decode_split_plan_lens(len(lens), hkv, arr if lens else None, cus,
+                                       ctypes.byref(ps), ctypes.byref(npart))
+    return st, ps.value, npart.value
+
+
+def _live(hkv, lens, ps):
+    return hkv * sum(-(-c // ps) for c in lens if c > 0)
+
+
+def test_split_plan_lens_mixed_batch(lib):
+    # hybrid full-attention decode: contexts 4097 and 8192, 2 KV heads.  The
+    # maximum-only plan takes 16 x 512 and leaves 56 of 256 workgroups
+    # without keys; from the lengths, 20 x 416 gives 240 live workgroups,
+    # and 384 would need 264.
+    lens = [4097, 8192] * 4
+    assert lplan(lib, 2, lens) == (OK, 416, 20)
+    assert _live(2, lens, 416) == 240 and _live(2, lens, 384) == 264
+
+
+def test_split_plan_lens_matches_uniform_plans(lib):
+    # with equal (or nearly equal) lengths the plan is the maximum-based one
+    assert lplan(lib, 8, [1084, 1038, 1106, 1094, 1090, 1110, 1061, 1068]) == (OK, 288, 4)
+    assert lplan(lib, 8, [8192] * 4) == (OK, 1024, 8)
+    assert lplan(lib, 8, [1100] * 64)[2] == 1          # 512 live items: no split
+    assert lplan(lib, 2, [50, 37]) == (OK, 64, 1)      # short contexts: one piece
+
+
+@pytest.mark.parametrize("hkv,lens", [(2, [4097, 8192] * 4), (8, [100, 9000, 20, 3000]),
+                                      (1, [1, 2, 3, 100000]), (4, [0, -5, 700, 0]),
+                                      (8, [1152] * 8 + [64] * 8), (2, [128])])
+def test_split_plan_lens_smallest_partition_within_the_cus(lib, hkv, lens):
+    st, ps, npart = lplan(lib, hkv, lens)
+    top = max(max(lens), 1)
+    assert st == OK
+    assert ps > 0 and ps % 16 == 0 and ps * npart >= top
+    if npart > 1:
+        assert ps % 32 == 0 and ps >= 128
+        assert ps * (npart - 1) < top
+        assert _live(hkv, lens, ps) <= 256
+        assert ps == 128 or _live(hkv, lens, ps - 32) > 256   # the smallest such size
+
+
+def test_split_plan_lens_validation(lib):
+    ps, npart = ctypes.c_int32(), ctypes.c_int32()
+    f = lib.pa_decode_split_plan_lens
+    arr = (ctypes.c_int32 * 2)(10, 20)
+    assert f(2, 1, None, 256, ctypes.byref(ps), ctypes.byref(npart)) == INVALID
+    assert f(2, 0, arr, 256, ctypes.byref(ps), ctypes.byref(npart)) == INVALID
+    assert f(2, 1, arr, 0, ctypes.byref(ps), ctypes.byref(npart)) == INVALID
+    assert f(-1, 1, arr, 256, ctypes.byref(ps), ctypes.byref(npart)) == INVALID
+    assert f(2, 1, arr, 256, None, ctypes.byref(npart)) == INVALID
+    assert lplan(lib, 4, []) == (OK, 16, 1)             # empty batch

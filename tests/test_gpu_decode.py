@@ -9,7 +9,7 @@ import oracle
 import paged_kv_gqa_write_amd as pa
 import workloads
 from _gpu_helpers import (DEV, announce, check_tolerance, decode_gpu, decode_oracle, gpu_f64)
-from _helpers import bits
+from _helpers import bits, contiguous_twin, permuted_case
 
 pytestmark = pytest.mark.gpu
 
@@ -176,3 +176,48 @@ def test_decode_repeat_runs_bitwise_identical():
     a = decode_gpu(case)
     b = decode_gpu(case)
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("ps,P", [(64, 1), (16, 3)], ids=["one_partition", "split"])
+def test_negative_context_gives_nan_in_every_plan(ps, P):
+    """A negative length is invalid device data: that sequence's output is
+    NaN whether the decode kernel writes it (one partition) or the reduce
+    combines split-K pieces; the others are unaffected."""
+    announce(f"decode negative context ps={ps} P={P}")
+    case = workloads.make_decode_case("neg", context_lens=[40, 40, 33], num_q_heads=8,
+                                      num_kv_heads=2, head_dim=128, num_blocks=16, seed=14)
+    ref = decode_oracle(case)
+    case.context_lens[1] = -5
+    case.slot_mapping[1] = -1
+    out = decode_gpu(case, partition_size=ps, num_partitions=P)
+    assert torch.isnan(out[1].float()).all()
+    check_tolerance(f"negative context, others (P={P})", out[[0, 2]], ref[[0, 2]])
+
+
+def test_decode_mixed_lengths_plan_parity():
+    """The hybrid batch (4097- and 8192-token contexts, 2 KV heads) in the
+    plan made from its actual lengths (20 partitions of 416 tokens: 240 live
+    workgroups instead of 200 with the maximum-based 16 x 512), at the
+    literal bar."""
+    announce("decode hybrid_decode_b8, plan from lengths")
+    case = workloads.hybrid_decode()
+    ps, P = pa.decode_split_plan_lens(case.num_kv_heads, case.context_lens)
+    assert (ps, P) == (416, 20)
+    out = decode_gpu(case, partition_size=ps, num_partitions=P)
+    check_tolerance("hybrid decode, plan from lengths", out, decode_oracle(case), literal=True)
+
+
+def test_block_permutation_and_contiguous_twin_bitwise_split_plan_from_lengths():
+    """Layout invariance of the mixed-length batch in its length-based plan."""
+    announce("decode permutation invariance, mixed lengths")
+    case = workloads.make_decode_case("permmix", context_lens=[4097, 300, 8192, 17],
+                                      num_q_heads=16, num_kv_heads=2, head_dim=256,
+                                      num_blocks=896, sigma=0.5, scale=1 / 16, seed=15)
+    ps, P = pa.decode_split_plan_lens(case.num_kv_heads, case.context_lens)
+    assert P > 1
+    base = decode_gpu(case, partition_size=ps, num_partitions=P)
+    assert torch.equal(decode_gpu(permuted_case(case, seed=2), partition_size=ps,
+                                  num_partitions=P).view(torch.int16), base.view(torch.int16))
+    assert torch.equal(decode_gpu(contiguous_twin(case), partition_size=ps,
+                                  num_partitions=P).view(torch.int16), base.view(torch.int16))
+    check_tolerance("mixed lengths", base, decode_oracle(case), literal=True)

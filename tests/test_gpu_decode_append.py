@@ -96,3 +96,33 @@ def test_decode_append_repeat_runs_bitwise_identical():
     a, _, _ = _append_gpu(case)
     b, _, _ = _append_gpu(case)
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("ps,P", [(64, 1), (16, 3)], ids=["one_partition", "split"])
+def test_decode_append_negative_context(ps, P):
+    """A negative length: NaN output for that sequence in every plan, and its
+    token is not written (the pools equal the oracle's write_kv of the other
+    sequences' tokens only)."""
+    announce(f"decode_append negative context ps={ps} P={P}")
+    case = workloads.make_decode_case("negapp", context_lens=[40, 40, 33], num_q_heads=8,
+                                      num_kv_heads=2, head_dim=128, num_blocks=16, seed=16)
+    ref = decode_oracle(case)
+    case.context_lens[1] = -5
+    case.slot_mapping[1] = -1
+    out, kc, vc = _append_gpu(case, ps, P)
+    assert torch.isnan(out[1].float()).all()
+    check_tolerance(f"append negative context, others (P={P})", out[[0, 2]], ref[[0, 2]])
+    okc, ovc = _oracle_pools(case)
+    assert np.array_equal(bits(kc), okc) and np.array_equal(bits(vc), ovc)
+
+
+def test_decode_append_mixed_lengths_plan_parity():
+    """The hybrid batch appended and decoded in the plan made from its
+    lengths (20 x 416), literal bar; pools bit-exact."""
+    announce("decode_append hybrid_decode_b8, plan from lengths")
+    case = workloads.hybrid_decode()
+    ps, P = pa.decode_split_plan_lens(case.num_kv_heads, case.context_lens)
+    out, kc, vc = _append_gpu(case, ps, P)
+    check_tolerance("append hybrid, plan from lengths", out, decode_oracle(case), literal=True)
+    okc, ovc = _oracle_pools(case)
+    assert np.array_equal(bits(kc), okc) and np.array_equal(bits(vc), ovc)

@@ -7,7 +7,7 @@ import oracle
 import workloads
 from _gpu_helpers import (announce, check_tolerance, decode_gpu, prefill_gpu, prefill_oracle,
                           prefill_oracle_pools)
-from _helpers import bits
+from _helpers import bits, contiguous_twin, permuted_case
 
 pytestmark = pytest.mark.gpu
 
@@ -23,25 +23,44 @@ def test_prefill_qwen3_4b_full_parity():
     check_tolerance("qwen3_4b prefill", out, prefill_oracle(case), literal=False)
 
 
-def _sampled_rows(n):
-    rows = list(range(0, 64)) + list(range(n // 2 - 8, n // 2 + 8)) + list(range(n - 40, n))
-    return sorted(set(r for r in rows if 0 <= r < n))
-
-
-def test_prefill_hybrid_4097_sampled_parity():
-    """One 4097-token prefill at head_dim 256: sampled rows, each computed by
-    the oracle as a decode of that token over its causal context (the oracle
-    invariant 'prefill row i = decode with context prefix+i+1')."""
-    announce("prefill hybrid_prefill_4097")
+def test_prefill_hybrid_4097_full_parity():
+    """One 4097-token prefill at head_dim 256 (16/2 heads, sigma 0.5): every
+    one of the 4097 x 16 x 256 outputs against the oracle.  Here the exact
+    result rounded to bf16 stays below the literal bound (floor ~3.9e-3),
+    so the literal 4e-3 max and 5e-4 mean are asserted; the report prints
+    both beside the floor."""
+    announce("prefill hybrid_prefill_4097 (all rows)")
     case = workloads.hybrid_prefill()
     out = prefill_gpu(case)
-    kc, vc = prefill_oracle_pools(case)
-    rows = _sampled_rows(case.total_q)
-    q = bits(case.q)
-    ref = np.stack([oracle.decode(q[r:r + 1], kc, vc, case.block_tables.numpy()[:1], [r + 1],
-                                  case.scale, case.num_q_heads, case.num_kv_heads)[0]
-                    for r in rows])
-    check_tolerance("hybrid prefill sampled", out[rows], ref, literal=False)
+    rep = check_tolerance("hybrid prefill 4097, all rows", out, prefill_oracle(case),
+                          literal=True)
+    assert rep["n"] == 4097 * 16 * 256
+
+
+def _unaligned_prefix_case():
+    # Qwen3-4B heads; prefixes that end inside a block, sequences ending
+    # mid-block, a sequence longer than one column slot per head group
+    return workloads.make_prefill_case("unaligned", q_lens=[300, 129, 64, 200],
+                                       prefix_lens=[77, 0, 500, 33], num_q_heads=32,
+                                       num_kv_heads=8, head_dim=128, num_blocks=256, seed=21)
+
+
+@pytest.mark.parametrize("which", ["qwen3_4b_prefill_4x1024", "unaligned_prefixes"])
+def test_prefill_block_permutation_and_contiguous_twin_bitwise(which):
+    """Where the blocks sit in the pool must not matter: the same prefill
+    with every physical block moved by a random permutation (table and
+    slots rewritten to match), and with each sequence's blocks laid out
+    contiguously from block 0, gives bit-identical outputs."""
+    announce(f"prefill permutation invariance {which}")
+    case = (workloads.qwen3_4b_prefill() if which == "qwen3_4b_prefill_4x1024"
+            else _unaligned_prefix_case())
+    base = prefill_gpu(case)
+    assert torch.equal(prefill_gpu(permuted_case(case, seed=5)).view(torch.int16),
+                       base.view(torch.int16))
+    assert torch.equal(prefill_gpu(contiguous_twin(case)).view(torch.int16),
+                       base.view(torch.int16))
+    if which == "unaligned_prefixes":
+        check_tolerance("unaligned prefixes", base, prefill_oracle(case), literal=False)
 
 
 @pytest.mark.parametrize("hq,hkv,d", [(4, 2, 64), (8, 8, 128), (32, 8, 128), (12, 4, 128),

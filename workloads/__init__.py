@@ -218,6 +218,26 @@ def make_decode_case(name, *, context_lens=None, ctx_range=None, batch=None,
                       ctx.to(torch.int32), bt, kc, vc, q, k_new, v_new, slots, sigma)
 
 
+def decode_layer(case: DecodeCase, seed: int, poison=True) -> DecodeCase:
+    """Another layer of the same decode step: the same lengths, block table
+    and slots, freshly drawn pools, queries and new-token K/V (generator
+    seeded with `seed`; draw order K pool -> V pool -> Q -> new-token K/V),
+    NaN-poisoned like the original."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    kc = _normal_bf16(g, tuple(case.k_cache.shape), case.sigma)
+    vc = _normal_bf16(g, tuple(case.v_cache.shape), case.sigma)
+    q = _normal_bf16(g, tuple(case.q.shape), case.sigma)
+    k_new = _normal_bf16(g, tuple(case.k_new.shape), case.sigma)
+    v_new = _normal_bf16(g, tuple(case.v_new.shape), case.sigma)
+    if poison:
+        poison_pool(kc, vc, case.block_tables,
+                    [int(c) - 1 if int(c) > 0 else 0 for c in case.context_lens])
+    return DecodeCase(f"{case.name}_layer{seed}", case.num_q_heads, case.num_kv_heads,
+                      case.head_dim, case.num_blocks, case.scale, case.context_lens.clone(),
+                      case.block_tables.clone(), kc, vc, q, k_new, v_new,
+                      case.slot_mapping.clone(), case.sigma)
+
+
 def make_prefill_case(name, *, q_lens, prefix_lens, num_q_heads, num_kv_heads, head_dim,
                       num_blocks, sigma=1.0, scale=None, seed=42, poison=True,
                       permute=True, max_blocks=None):
