@@ -74,7 +74,8 @@ typedef enum {
   PA_ERR_INVALID_ARG = -1,  /* null pointer, negative size, inconsistent sizes */
   PA_ERR_UNSUPPORTED = -2,  /* head_dim / group / block_size outside the supported set */
   PA_ERR_LAUNCH = -3,       /* the HIP runtime rejected a kernel launch */
-  PA_ERR_NO_MEMORY = -4     /* host allocation failed (prefix index only) */
+  PA_ERR_NO_MEMORY = -4,    /* host allocation failed (prefix index only) */
+  PA_ERR_TOO_LARGE = -5     /* split-K pieces exceed the static scratch (pa_decode_noalloc) */
 } pa_status;
 
 /*
@@ -161,6 +162,31 @@ int pa_decode_append(void* out, float* part_out, float* part_lse,
                      int32_t head_dim, int32_t block_size, int64_t num_blocks,
                      int32_t max_blocks_per_seq, int32_t partition_size,
                      int32_t num_partitions, float scale, void* stream);
+
+/*
+ * pa_decode_noalloc -- pa_decode followed (when num_partitions > 1) by
+ * pa_decode_reduce, with no workspace argument and no allocation: for
+ * callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * split-K pieces live in a static device array of the library (16 MiB per
+ * GPU, held until the process ends): B * Hq * num_partitions pieces of
+ * D + 1 floats (the pieces rounded up to 256 bytes, then the LSEs) must fit,
+ * else PA_ERR_TOO_LARGE and nothing is enqueued.  Every call on a GPU shares
+ * that GPU's array, so calls that overlap on one GPU (another stream, another
+ * host thread) race; calls on one stream are ordered.  Writes out[s, h, :]
+ * (bf16), bit for bit what pa_decode (+ pa_decode_reduce with the same
+ * context_lens) writes.  The first call on a device with num_partitions > 1
+ * looks up that device's copy of the array (PA_ERR_LAUNCH if that fails).
+ *
+ *   out            device, bf16 [num_seqs, Hq, D] (required)
+ *   other arguments as for pa_decode.
+ */
+int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                      int32_t max_blocks_per_seq, int32_t partition_size,
+                      int32_t num_partitions, float scale, void* stream);
 
 /*
  * pa_decode_reduce -- log-sum-exp combination of pa_decode's split-K pieces:

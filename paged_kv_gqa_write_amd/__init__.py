@@ -20,7 +20,7 @@ __all__ = [
     "PAError", "load_library", "library_path", "write_kv", "decode", "decode_partials",
     "decode_reduce", "decode_append", "decode_multi", "decode_multi_partials", "decode_multi_reduce", "prefill",
     "copy_blocks", "PrefixIndex", "decode_split_plan", "decode_split_plan_lens",
-    "decode_multi_split_plan", "status_string", "EXPORTED_SYMBOLS",
+    "decode_multi_split_plan", "decode_noalloc", "status_string", "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -29,6 +29,7 @@ _lib = None
 
 BLOCK_SIZE = 16
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_LAUNCH, PA_ERR_NO_MEMORY = 0, -1, -2, -3, -4
+PA_ERR_TOO_LARGE = -5
 
 _vp, _i32, _i64, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
 _pi32 = ctypes.POINTER(ctypes.c_int32)
@@ -40,6 +41,8 @@ _SIGNATURES = {
     "pa_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                  _i32, _i64, _i32, _i32, _i32, _f32, _vp]),
     "pa_decode_reduce": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pa_decode_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                         _i32, _i64, _i32, _i32, _i32, _f32, _vp]),
     "pa_decode_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                         _i32, _i32, _i32, _i32, _i64, _i32, _i32, _i32, _f32,
                                         _vp]),
@@ -372,6 +375,28 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, *, max_contex
     part_out, part_lse = decode_partials(q, k_cache, v_cache, block_tables, context_lens, scale,
                                          ps, P, part_out, part_lse)
     return decode_reduce(part_out, part_lse, context_lens, ps, out=out)
+
+
+def decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale, partition_size,
+                   num_partitions, out=None):
+    """Decode (+ the reduce when num_partitions > 1) with the split-K pieces in
+    the library's static per-GPU scratch instead of a workspace: nothing is
+    allocated by the library (pa_decode_noalloc).  Calls that overlap on one
+    GPU race on that scratch.  -> bf16 [B, Hq, D]"""
+    _need(q, "q", torch.bfloat16, 3)
+    B, hq, d = q.shape
+    _need_shape(out, "out", torch.bfloat16, (B, hq, d))
+    if out is None:
+        out = torch.empty(B, hq, d, dtype=torch.bfloat16, device=q.device)
+    B, hq, hkv, d, nb = _decode_checks(q, k_cache, v_cache, block_tables, context_lens, 0, out,
+                                       None, None, 1)
+    st = load_library().pa_decode_noalloc(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(),
+                                          v_cache.data_ptr(), block_tables.data_ptr(),
+                                          context_lens.data_ptr(), B, hq, hkv, d, BLOCK_SIZE, nb,
+                                          block_tables.shape[1], int(partition_size),
+                                          int(num_partitions), float(scale), _stream(q.device))
+    _check(st, "pa_decode_noalloc")
+    return out
 
 
 def decode_append(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, *,

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libpa.so")
 SOURCES = ["pa_api.hip", "write_kv.hip", "decode.hip", "prefill.hip", "copy.hip",
-           "prefix_index.cpp"]
+           "noalloc.hip", "prefix_index.cpp"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

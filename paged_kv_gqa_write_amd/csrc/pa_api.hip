@@ -83,12 +83,14 @@ int pa_write_kv(const void* k_new, const void* v_new, const int64_t* slot_mappin
                              num_kv_heads, head_dim, num_blocks, as_stream(stream));
 }
 
-int pa_decode_multi(void* out, float* part_out, float* part_lse, const void* q,
-                    const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                    const int32_t* context_lens, int32_t num_seqs, int32_t query_len,
-                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                    int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
-                    int32_t partition_size, int32_t num_partitions, float scale, void* stream) {
+}  // extern "C"
+
+namespace pa {
+
+int validate_decode(int32_t num_seqs, int32_t query_len, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                    int64_t num_blocks, int32_t max_blocks_per_seq, int32_t partition_size,
+                    int32_t num_partitions, float scale) {
   if (num_seqs < 0 || num_blocks < 0) return PA_ERR_INVALID_ARG;
   if (query_len < 1) return PA_ERR_INVALID_ARG;
   if (query_len > kMaxQueryLen) return PA_ERR_UNSUPPORTED;
@@ -105,6 +107,23 @@ int pa_decode_multi(void* out, float* part_out, float* part_lse, const void* q,
   if ((int64_t)num_partitions * num_kv_heads * num_seqs * chunks > kMaxGrid)
     return PA_ERR_UNSUPPORTED;
   if ((int64_t)num_seqs * query_len * num_q_heads > kMaxGrid) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+}  // namespace pa
+
+extern "C" {
+
+int pa_decode_multi(void* out, float* part_out, float* part_lse, const void* q,
+                    const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t query_len,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
+                    int32_t partition_size, int32_t num_partitions, float scale, void* stream) {
+  const int st = pa::validate_decode(num_seqs, query_len, num_q_heads, num_kv_heads, head_dim,
+                                     block_size, num_blocks, max_blocks_per_seq, partition_size,
+                                     num_partitions, scale);
+  if (st != PA_OK) return st;
   if (num_seqs == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
   if (num_partitions == 1 && !out) return PA_ERR_INVALID_ARG;
@@ -362,6 +381,8 @@ const char* pa_status_string(int status) {
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: unsupported shape";
     case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: kernel launch failed";
     case PA_ERR_NO_MEMORY: return "PA_ERR_NO_MEMORY: host allocation failed";
+    case PA_ERR_TOO_LARGE:
+      return "PA_ERR_TOO_LARGE: split-K pieces exceed the library's static scratch";
     default: return "unknown pa_status";
   }
 }

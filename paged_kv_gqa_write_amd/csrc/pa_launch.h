@@ -9,6 +9,13 @@
 
 namespace pa {
 
+// Host checks shared by the decode entry points (everything except the
+// pointer arguments): returns PA_OK or the pa_status to report.
+int validate_decode(int32_t num_seqs, int32_t query_len, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                    int64_t num_blocks, int32_t max_blocks_per_seq, int32_t partition_size,
+                    int32_t num_partitions, float scale);
+
 int launch_write_kv(const void* k_new, const void* v_new, const int64_t* slot_mapping,
                     void* k_cache, void* v_cache, int num_tokens, int num_kv_heads,
                     int head_dim, int64_t num_blocks, hipStream_t stream);

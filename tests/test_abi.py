@@ -35,7 +35,7 @@ def test_header_declares_the_boundary():
                                          "pa_decode_append",
                                          "pa_prefill", "pa_copy_blocks",
                                          "pa_decode_split_plan", "pa_decode_multi_split_plan",
-                                         "pa_decode_split_plan_lens",
+                                         "pa_decode_split_plan_lens", "pa_decode_noalloc",
                                          "pa_status_string",
                                          "pa_prefix_index_create", "pa_prefix_index_destroy",
                                          "pa_prefix_index_size", "pa_prefix_index_match",
@@ -63,7 +63,8 @@ def test_missing_library_fails_loudly(tmp_path):
 
 
 def test_status_strings(lib):
-    for code in (OK, INVALID, UNSUPPORTED, pa.PA_ERR_LAUNCH, pa.PA_ERR_NO_MEMORY):
+    for code in (OK, INVALID, UNSUPPORTED, pa.PA_ERR_LAUNCH, pa.PA_ERR_NO_MEMORY,
+                 pa.PA_ERR_TOO_LARGE):
         s = lib.pa_status_string(code).decode()
         assert s.startswith("PA_")
     assert "unknown" in lib.pa_status_string(7).decode()
@@ -432,3 +433,28 @@ def test_split_plan_lens_validation(lib):
     assert f(-1, 1, arr, 256, ctypes.byref(ps), ctypes.byref(npart)) == INVALID
     assert f(2, 1, arr, 256, None, ctypes.byref(npart)) == INVALID
     assert lplan(lib, 4, []) == (OK, 16, 1)             # empty batch
+
+
+def _noalloc(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, ctx=FAKE, B=8, hq=32, hkv=8, d=128,
+             bs=16, nb=4096, mb=72, ps=288, P=4, scale=0.088)
+    a.update(kw)
+    return lib.pa_decode_noalloc(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["ctx"], a["B"],
+                                 a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["mb"], a["ps"],
+                                 a["P"], a["scale"], None)
+
+
+def test_decode_noalloc_validation(lib):
+    assert _noalloc(lib, B=-1) == INVALID
+    assert _noalloc(lib, hq=30) == INVALID
+    assert _noalloc(lib, d=80) == UNSUPPORTED
+    assert _noalloc(lib, ps=100) == INVALID
+    assert _noalloc(lib, P=0) == INVALID
+    assert _noalloc(lib, ps=1 << 24, P=4096) == UNSUPPORTED
+    assert _noalloc(lib, scale=-1.0) == INVALID
+    assert _noalloc(lib, out=None) == INVALID           # out is always written
+    assert _noalloc(lib, ctx=None) == INVALID
+    assert _noalloc(lib, B=0, out=None, q=None, kc=None, vc=None, bt=None, ctx=None) == OK
+    # pieces beyond the 16 MiB static scratch: B*Hq*P*(D+1)*4 bytes
+    assert _noalloc(lib, B=64, hq=64, P=8, ps=1024) == pa.PA_ERR_TOO_LARGE   # 16.5 MiB
+    assert _noalloc(lib, B=4, hq=64, hkv=8, d=256, P=64, ps=128) == pa.PA_ERR_TOO_LARGE
