@@ -15,6 +15,9 @@ Cache holds.  `value` = the step's KV bytes / step time.
 The other workloads are legs of the same JSON line, each with its own
 roofline object for its dominant kernel:
   qwen3_32b_decode_b4_8192  batch 4 at 8192 tokens: split-K + reduce, 64 layers
+  qwen3_32b_decode_mixed_b8 one 8192-token request among seven of 1024-1152:
+                            split plan from the batch's lengths (live work
+                            ranked first), beside the plan from the longest
   hybrid_decode_b8          16/2 heads, head_dim 256, contexts 4097/8192, plan
                             from the batch's lengths; 16 layers' pools
   hybrid_prefill_4097       one 4097-token causal prefill (16/2/256); 16 layers
@@ -45,7 +48,8 @@ METRIC = "paged GQA decode KV GB/s (% of HBM peak); prefill TFLOP/s (% of MFMA p
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
 HEADLINE = "qwen3_32b_decode_b64"
-LEGS = [HEADLINE, "qwen3_32b_decode_b4_8192", "hybrid_decode_b8", "hybrid_prefill_4097",
+LEGS = [HEADLINE, "qwen3_32b_decode_b4_8192", "qwen3_32b_decode_mixed_b8", "hybrid_decode_b8",
+        "hybrid_prefill_4097",
         "qwen3_4b_decode_b8", "qwen3_4b_prefill_4x1024", "write_kv", "verify", "kv_restore",
         "prefix_match"]
 DECODE_SOURCES = ["decode.hip", "pa_device.h"]
@@ -155,7 +159,7 @@ def roofline_mfma(flops, us, kernel, leg):
             "algorithmic_flops_per_launch": int(flops), "avg_launch_us": round(us, 3)}
 
 
-def decode_leg(c, name, case, layers, plan_from_lengths, detail=False):
+def decode_leg(c, name, case, layers, plan_from_lengths, detail=False, compare_max_plan=False):
     """One decode step = for every layer, pa_decode_append (append each
     sequence's new token and decode) and, with more than one partition,
     pa_decode_reduce.  Reports the step rate and the appending decode
@@ -215,15 +219,32 @@ def decode_leg(c, name, case, layers, plan_from_lengths, detail=False):
     if P > 1:
         red_us = c.per_call_ms(reduce, args.steps * L) * 1e3
         res["reduce_avg_launch_us"] = round(red_us, 3)
+    if compare_max_plan:
+        mps, mP = c.pa.decode_split_plan(B, hkv, int(case.context_lens.max()), c.cus)
+        mpo = torch.empty(B, hq, mP, d, dtype=torch.float32, device=dev)
+        mpl = torch.empty(B, hq, mP, dtype=torch.float32, device=dev)
+
+        def append_decode_max(i):
+            ok(lib.pa_decode_append(out.data_ptr(), mpo.data_ptr(), mpl.data_ptr(), q.data_ptr(),
+                                    k_new.data_ptr(), v_new.data_ptr(), kc[i % L].data_ptr(),
+                                    vc[i % L].data_ptr(), bt.data_ptr(), ctx.data_ptr(), B, hq,
+                                    hkv, d, 16, nb, mb, mps, mP, case.scale, sptr),
+               "pa_decode_append")
+
+        append_decode_max(0)
+        m_us = c.per_call_ms(append_decode_max, args.steps * L) * 1e3
+        res["plan_from_longest"] = {"partition_size": mps, "num_partitions": mP,
+                                    "kernel_avg_launch_us": round(m_us, 3),
+                                    "frac": round(kvb / (m_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
     if detail:
         layer_us = ms * 1e3 / L
         red_us = res.get("reduce_avg_launch_us", 0.0)
         res["per_layer_us"] = {
-            "step_per_layer": round(layer_us, 3), "decode_kernel": round(dec_us, 3),
-            "reduce_kernel": round(red_us, 3),
-            "rest": round(layer_us - dec_us - red_us, 3),
-            "note": "kernel averages from back-to-back launches; rest = launch gaps between "
-                    "the step's dependent kernels"}
+            "step_per_layer": round(layer_us, 3), "decode_kernel_back_to_back": round(dec_us, 3),
+            "reduce_kernel_back_to_back": round(red_us, 3),
+            "note": "kernel averages from back-to-back launches of one kernel; the split of "
+                    "the step itself (kernel durations and the gaps between them) comes from "
+                    "the rocprofv3 kernel trace"}
         # the same step captured once as a HIP graph and replayed
         side = torch.cuda.Stream(device=dev)
         side.wait_stream(c.stream)
@@ -538,6 +559,10 @@ def main():
     run("qwen3_32b_decode_b4_8192",
         lambda: decode_leg(c, "qwen3_32b_decode_b4_8192",
                            workloads.qwen3_32b_decode_long(poison=False), 64, True))
+    run("qwen3_32b_decode_mixed_b8",
+        lambda: decode_leg(c, "qwen3_32b_decode_mixed_b8",
+                           workloads.qwen3_32b_decode_mixed(poison=False), 64, True,
+                           compare_max_plan=True))
     run("hybrid_decode_b8",
         lambda: decode_leg(c, "hybrid_decode_b8", workloads.hybrid_decode(poison=False), 16,
                            True))

@@ -337,15 +337,20 @@ int pa_decode_split_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t max_con
  * pa_decode_split_plan_lens -- host-only helper: the same plan from the
  * batch's actual context lengths (context_lens: HOST int32 [num_seqs], may
  * be NULL when num_seqs == 0).  pa_decode launches one workgroup per
- * (partition, KV head, sequence); those whose partition starts past their
- * sequence's length exit at once.  The plan takes the smallest partition
- * (whole 32-key pairs, at least 128 keys) whose live workgroups number at
- * most num_compute_units, so that in a batch of mixed lengths the long
- * sequences get more partitions; when one partition per sequence already
- * gives at least num_compute_units live workgroups, one partition of the
- * longest context (rounded up to 16).  Writes *partition_size (multiple of
- * 16) and *num_partitions, covering the longest context; returns PA_OK or
- * PA_ERR_INVALID_ARG.
+ * (partition, KV head, sequence); with up to 64 sequences it launches those
+ * whose partition holds keys first and the empty ones (past their
+ * sequence's length) last.  The plan takes the smallest partition (whole
+ * 32-key pairs, at least 128 keys) whose live workgroups number at most
+ * num_compute_units, so that in a batch of mixed lengths the long sequences
+ * get more partitions; when one partition per sequence already gives at
+ * least num_compute_units live workgroups, one partition of the longest
+ * context (rounded up to 16).  That plan is taken only when its partition
+ * is at most 2/3 of the one pa_decode_split_plan gives for the longest
+ * context (a launch of more than one workgroup per compute unit pays one
+ * extra memory round trip for the ranking); otherwise, and for more than 64
+ * sequences, the result is pa_decode_split_plan's.  Writes *partition_size
+ * (multiple of 16) and *num_partitions, covering the longest context;
+ * returns PA_OK or PA_ERR_INVALID_ARG.
  */
 int pa_decode_split_plan_lens(int32_t num_seqs, int32_t num_kv_heads,
                               const int32_t* context_lens, int32_t num_compute_units,

@@ -33,6 +33,8 @@
 // bf16 hi/lo pair (two products), which keeps its rounding error far below
 // the bf16 output rounding; decode is memory-bound, so the extra products
 // cost no time.  Waves are merged through LDS.
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -203,15 +205,27 @@ __device__ __forceinline__ void patch_pair(PairRegs<D>& r, const u32x4 (&newk)[D
 // or may not have been written yet), and wave 0 of the workgroup whose
 // partition holds ctx-1 writes the row into the pools.  k_pool/v_pool are
 // the same pools as k_cache/v_cache; no reader depends on those stores.
-template <int D, int NW, int NBUF, int NT, bool APPEND>
+//
+// COMPACT (split launches of up to 64 sequences that need more than one
+// dispatch round): items are ranked so that those holding keys come first
+// and the empty ones (partitions past a sequence's length) last, so that
+// every item with work is dispatched in the first round.  An empty
+// workgroup still waits for its own small loads behind the batch's KV
+// stream, and a live one dispatched after it would start that much later.
+// Lane i loads sequence i's length; sequence s has n_s = min(ceil(ctx/ps),
+// P) live partitions, and its live items come in the order (KV head,
+// partition), as its empty ones do.  When every sequence fills every
+// partition this is the plain order.
+template <int D, int NW, int NBUF, int NT, bool APPEND, bool COMPACT>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(
     uint16_t* __restrict__ out, float* __restrict__ part_out, float* __restrict__ part_lse,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, const uint16_t* __restrict__ k_new,
-    const uint16_t* __restrict__ v_new, uint16_t* k_pool, uint16_t* v_pool, int query_len,
-    int num_q_heads, int num_kv_heads, int group, int64_t num_blocks, int max_blocks,
-    int blocks_per_part, int num_partitions, int num_chunks, float scale_log2) {
+    const uint16_t* __restrict__ v_new, uint16_t* k_pool, uint16_t* v_pool, int num_seqs,
+    int query_len, int num_q_heads, int num_kv_heads, int group, int64_t num_blocks,
+    int max_blocks, int blocks_per_part, int num_partitions, int num_chunks,
+    float scale_log2) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   int item = blockIdx.x, chunk = 0;
@@ -223,13 +237,38 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
     chunk = r / width;
     item = base + r % width;
   }
-  const int p = item % num_partitions;
-  const int g = (item / num_partitions) % num_kv_heads;
-  const int s = item / (num_partitions * num_kv_heads);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int col = lane & 15;
   const int c = lane >> 4;
+  // Items are (sequence, KV head, partition), partition fastest.
+  int p = item % num_partitions;
+  int g = (item / num_partitions) % num_kv_heads;
+  int s = item / (num_partitions * num_kv_heads);
+  int cl = 0;  // COMPACT: lane i holds sequence i's length
+  if constexpr (COMPACT) {
+    cl = context_lens[min(lane, num_seqs - 1)];
+    const int ps = blocks_per_part * kBlock;
+    const int n = lane < num_seqs
+                      ? (cl <= 0 ? 0 : (int)min((int64_t)num_partitions,
+                                               ((int64_t)cl + ps - 1) / ps))
+                      : 0;
+    const int live = wave_total(n) * num_kv_heads;
+    // Item `item` among the live items or among the empty ones.
+    const bool in_live = item < live;
+    const int per = in_live ? n : (lane < num_seqs ? num_partitions - n : 0);
+    const int rr = in_live ? item : item - live;
+    const int cnt = per * num_kv_heads;
+    const int incl = wave_inclusive_scan(cnt);
+    const uint64_t hit = __ballot(incl > rr);
+    if (hit != 0) {  // always: the counts add up to the launch's items
+      s = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
+      const int off = rr - __builtin_amdgcn_readlane(incl - cnt, s);
+      const int per1 = __builtin_amdgcn_readlane(per, s);  // > 0: s holds item rr
+      g = off / per1;
+      p = (in_live ? 0 : __builtin_amdgcn_readlane(n, s)) + off - g * per1;
+    }
+  }
 
   // Wave w takes the contiguous pair range [k0, k0+nk) of the partition.
   // The range comes from the partition size alone, so the block-table entries
@@ -249,7 +288,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
   };
   load_entries(0);
 
-  const int ctx = context_lens[s];
+  const int ctx = COMPACT ? __builtin_amdgcn_readlane(cl, s) : context_lens[s];
   const int nblk = ctx > 0 ? (int)(((int64_t)ctx + kBlock - 1) / kBlock) : 0;
   bool bad = ctx < 0 || nblk > max_blocks ||
              (int64_t)ctx > (int64_t)num_partitions * blocks_per_part * kBlock ||
@@ -571,33 +610,43 @@ int launch_decode(void* out, float* part_out, float* part_lse, const void* q,
   if (nwg > 0x7FFFFFFF) return -2;
   const float scale_log2 = scale * kLog2e;
   const int bpp = partition_size / kBlock;
-  // Waves per workgroup and pairs in flight per wave.  head_dim 128: 3 waves,
+  // Ranked launch order (COMPACT) when a split launch of up to 64 sequences
+  // needs more than one workgroup per compute unit (the kernel ranks one
+  // sequence per lane); otherwise the plain order.
+  const bool compact = num_partitions > 1 && num_seqs <= 64 && nwg > kComputeUnits;
+  auto go = [&](auto kern, int nw) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(nw * 64), 0, stream, (uint16_t*)out,
+                       part_out, part_lse, (const uint16_t*)q, (const uint16_t*)k_cache,
+                       (const uint16_t*)v_cache, block_tables, context_lens,
+                       (const uint16_t*)k_new, (const uint16_t*)v_new, (uint16_t*)k_cache,
+                       (uint16_t*)v_cache, num_seqs, query_len, num_q_heads, num_kv_heads,
+                       group, num_blocks, max_blocks_per_seq, bpp, num_partitions, chunks,
+                       scale_log2);
+  };
+  // Waves per workgroup (3 or 4) and pairs in flight per wave.  head_dim 128: 3 waves,
   // so that with partitions of 9 pairs (the batch-8 plans) every wave takes
   // exactly 3 pairs (two-tile form, Qwen3-4B verify batch 8: 13.8 -> 13.1 us,
   // 12.8 with 2 pairs in flight).  The plain form keeps 2 pairs in flight
   // per wave (Qwen3-4B batch 8: 11.4 -> 10.1 us against 4 waves with 1 pair
   // in flight); the appending form keeps 1 (11.2 -> 10.8 us; with 2 its
   // register patching makes the compiler wait for both pairs).
-  auto go = [&](auto kern, int nw) {
-    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(nw * 64), 0, stream, (uint16_t*)out,
-                       part_out, part_lse, (const uint16_t*)q, (const uint16_t*)k_cache,
-                       (const uint16_t*)v_cache, block_tables, context_lens,
-                       (const uint16_t*)k_new, (const uint16_t*)v_new, (uint16_t*)k_cache,
-                       (uint16_t*)v_cache, query_len, num_q_heads, num_kv_heads, group,
-                       num_blocks, max_blocks_per_seq, bpp, num_partitions, chunks, scale_log2);
+  auto pick = [&](auto compact_tag) {
+    constexpr bool C = decltype(compact_tag)::value;
+    switch (head_dim * 8 + nt * 2 + (append ? 1 : 0)) {
+      case 64 * 8 + 2: go(decode_kernel<64, 4, 4, 1, false, C>, 4); return 0;
+      case 64 * 8 + 4: go(decode_kernel<64, 4, 4, 2, false, C>, 4); return 0;
+      case 64 * 8 + 3: go(decode_kernel<64, 4, 4, 1, true, C>, 4); return 0;
+      case 128 * 8 + 2: go(decode_kernel<128, 3, 2, 1, false, C>, 3); return 0;
+      case 128 * 8 + 4: go(decode_kernel<128, 3, 2, 2, false, C>, 3); return 0;
+      case 128 * 8 + 3: go(decode_kernel<128, 3, 1, 1, true, C>, 3); return 0;
+      case 256 * 8 + 2: go(decode_kernel<256, 4, 2, 1, false, C>, 4); return 0;
+      case 256 * 8 + 4: go(decode_kernel<256, 4, 1, 2, false, C>, 4); return 0;
+      case 256 * 8 + 3: go(decode_kernel<256, 4, 2, 1, true, C>, 4); return 0;
+      default: return -2;
+    }
   };
-  switch (head_dim * 8 + nt * 2 + (append ? 1 : 0)) {
-    case 64 * 8 + 2: go(decode_kernel<64, 4, 4, 1, false>, 4); break;
-    case 64 * 8 + 4: go(decode_kernel<64, 4, 4, 2, false>, 4); break;
-    case 64 * 8 + 3: go(decode_kernel<64, 4, 4, 1, true>, 4); break;
-    case 128 * 8 + 2: go(decode_kernel<128, 3, 2, 1, false>, 3); break;
-    case 128 * 8 + 4: go(decode_kernel<128, 3, 2, 2, false>, 3); break;
-    case 128 * 8 + 3: go(decode_kernel<128, 3, 1, 1, true>, 3); break;
-    case 256 * 8 + 2: go(decode_kernel<256, 4, 2, 1, false>, 4); break;
-    case 256 * 8 + 4: go(decode_kernel<256, 4, 1, 2, false>, 4); break;
-    case 256 * 8 + 3: go(decode_kernel<256, 4, 2, 1, true>, 4); break;
-    default: return -2;
-  }
+  const int rc = compact ? pick(std::true_type{}) : pick(std::false_type{});
+  if (rc != 0) return rc;
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

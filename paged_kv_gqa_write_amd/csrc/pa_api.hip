@@ -284,8 +284,16 @@ int pa_decode_split_plan_lens(int32_t num_seqs, int32_t num_kv_heads,
   if (!partition_size || !num_partitions) return PA_ERR_INVALID_ARG;
   if (num_seqs < 0 || num_kv_heads <= 0 || num_compute_units <= 0) return PA_ERR_INVALID_ARG;
   if (num_seqs > 0 && !context_lens) return PA_ERR_INVALID_ARG;
-  // A launch holds one workgroup per (partition, KV head, sequence); the
-  // ones whose partition lies past their sequence's length exit at once.
+  int64_t max_ctx = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) max_ctx = std::max<int64_t>(max_ctx, context_lens[s]);
+  // Beyond 64 sequences the decode kernel keeps the plain launch order, in
+  // which empty workgroups may sit ahead of live ones: plan from the longest.
+  if (num_seqs > 64)
+    return pa_decode_split_plan(num_seqs, num_kv_heads, (int32_t)max_ctx, num_compute_units,
+                                partition_size, num_partitions);
+  // A launch holds one workgroup per (partition, KV head, sequence); with up
+  // to 64 sequences the decode kernel ranks the ones whose partition holds
+  // keys first, and the empty ones (past their sequence's length) after them.
   // The longest workgroup sets the launch time, so take the smallest
   // partition (whole 32-key pairs, at least 4 of them) whose live
   // workgroups still fit one per compute unit, counted over the actual
@@ -293,8 +301,6 @@ int pa_decode_split_plan_lens(int32_t num_seqs, int32_t num_kv_heads,
   // sequences more partitions instead of leaving compute units idle.
   constexpr int64_t kPair = 32;
   constexpr int64_t kMinPart = 4 * kPair;
-  int64_t max_ctx = 0;
-  for (int32_t s = 0; s < num_seqs; ++s) max_ctx = std::max<int64_t>(max_ctx, context_lens[s]);
   const int64_t ctx = max_ctx > 0 ? max_ctx : 1;
   auto live = [&](int64_t ps) {
     int64_t n = 0;
@@ -319,6 +325,18 @@ int pa_decode_split_plan_lens(int32_t num_seqs, int32_t num_kv_heads,
     ps = kPair * hi;
     np = (ctx + ps - 1) / ps;
     if (np == 1) ps = whole;
+  }
+  // A workgroup's time follows its partition's length in whole pairs per
+  // wave, while a launch beyond one dispatch round pays for the ranking (a
+  // second round trip before the K/V stream): keep the plan from the longest
+  // context unless the lengths allow a substantially shorter partition.
+  int32_t max_ps = 0, max_np = 0;
+  const int rc = pa_decode_split_plan(num_seqs, num_kv_heads, (int32_t)max_ctx,
+                                      num_compute_units, &max_ps, &max_np);
+  if (rc != PA_OK) return rc;
+  if (3 * ps > 2 * (int64_t)max_ps) {
+    ps = max_ps;
+    np = max_np;
   }
   if (ps > 0x7FFFFFF0LL) return PA_ERR_INVALID_ARG;
   *partition_size = (int32_t)ps;

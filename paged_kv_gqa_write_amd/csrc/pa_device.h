@@ -76,4 +76,50 @@ __device__ __forceinline__ T* uniform_ptr(T* p) {
   return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
 }
 
+// Sum, max and inclusive prefix sum over the 64 lanes of a wave with DPP row
+// operations (a few cycles each, no LDS crossbar).  The values are >= 0, so
+// 0 serves as the identity for lanes a row mask leaves out.  Sum and max
+// leave the total in lane 63.
+__device__ __forceinline__ int dpp(int v, int ctrl, int row_mask) {
+  switch (ctrl) {  // the control is an immediate
+    case 0xB1: return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+    case 0x4E: return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+    case 0x141: return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+    case 0x140: return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);
+    case 0x111: return __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);
+    case 0x112: return __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);
+    case 0x114: return __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);
+    case 0x118: return __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);
+    case 0x142: return __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);
+    default: return __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);
+  }
+}
+__device__ __forceinline__ int wave_total(int v) {
+  v += dpp(v, 0xB1, 0xF);   // quad_perm [1,0,3,2]
+  v += dpp(v, 0x4E, 0xF);   // quad_perm [2,3,0,1]
+  v += dpp(v, 0x141, 0xF);  // row_half_mirror
+  v += dpp(v, 0x140, 0xF);  // row_mirror: every lane holds its row's sum
+  v += dpp(v, 0x142, 0xA);  // row_bcast15 into rows 1 and 3
+  v += dpp(v, 0x143, 0xC);  // row_bcast31 into rows 2 and 3
+  return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ int wave_max_nonneg(int v) {
+  v = max(v, dpp(v, 0xB1, 0xF));
+  v = max(v, dpp(v, 0x4E, 0xF));
+  v = max(v, dpp(v, 0x141, 0xF));
+  v = max(v, dpp(v, 0x140, 0xF));
+  v = max(v, dpp(v, 0x142, 0xA));
+  v = max(v, dpp(v, 0x143, 0xC));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += dpp(v, 0x111, 0xF);  // row_shr:1
+  v += dpp(v, 0x112, 0xF);  // row_shr:2
+  v += dpp(v, 0x114, 0xF);  // row_shr:4
+  v += dpp(v, 0x118, 0xF);  // row_shr:8: scan within each row of 16
+  v += dpp(v, 0x142, 0xA);  // rows 1 and 3 add the previous row's total
+  v += dpp(v, 0x143, 0xC);  // rows 2 and 3 add the total of rows 0-1
+  return v;
+}
+
 }  // namespace pa

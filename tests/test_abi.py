@@ -391,13 +391,16 @@ def _live(hkv, lens, ps):
 
 
 def test_split_plan_lens_mixed_batch(lib):
-    # hybrid full-attention decode: contexts 4097 and 8192, 2 KV heads.  The
-    # maximum-only plan takes 16 x 512 and leaves 56 of 256 workgroups
-    # without keys; from the lengths, 20 x 416 gives 240 live workgroups,
-    # and 384 would need 264.
-    lens = [4097, 8192] * 4
-    assert lplan(lib, 2, lens) == (OK, 416, 20)
-    assert _live(2, lens, 416) == 240 and _live(2, lens, 384) == 264
+    # One 8192-token request among seven of ~1100 (8 KV heads): the longest
+    # alone gives 4 x 2048 (the long sequence's 32 workgroups each stream
+    # 2048 tokens); from the lengths, 15 x 576 keeps 232 live workgroups.
+    lens = [8192, 1084, 1038, 1106, 1094, 1090, 1110, 1061]
+    assert lplan(lib, 8, lens) == (OK, 576, 15)
+    assert _live(8, lens, 576) == 232 and _live(8, lens, 544) > 256
+    # hybrid contexts 4097 / 8192 (2 KV heads): 20 x 416 is the smallest
+    # partition within the CUs, but 416 > 2/3 * 512 -- the plan from the
+    # longest context (16 x 512, one dispatch round) is kept.
+    assert lplan(lib, 2, [4097, 8192] * 4) == (OK, 512, 16)
 
 
 def test_split_plan_lens_matches_uniform_plans(lib):
@@ -406,21 +409,27 @@ def test_split_plan_lens_matches_uniform_plans(lib):
     assert lplan(lib, 8, [8192] * 4) == (OK, 1024, 8)
     assert lplan(lib, 8, [1100] * 64)[2] == 1          # 512 live items: no split
     assert lplan(lib, 2, [50, 37]) == (OK, 64, 1)      # short contexts: one piece
+    assert lplan(lib, 8, [100] * 70 + [8192]) == plan(lib, 71, 8, 8192)   # > 64 sequences
 
 
 @pytest.mark.parametrize("hkv,lens", [(2, [4097, 8192] * 4), (8, [100, 9000, 20, 3000]),
                                       (1, [1, 2, 3, 100000]), (4, [0, -5, 700, 0]),
-                                      (8, [1152] * 8 + [64] * 8), (2, [128])])
-def test_split_plan_lens_smallest_partition_within_the_cus(lib, hkv, lens):
+                                      (8, [1152] * 8 + [64] * 8), (2, [128]),
+                                      (8, [8192, 100, 100, 100])])
+def test_split_plan_lens_shorter_partition_within_the_cus(lib, hkv, lens):
     st, ps, npart = lplan(lib, hkv, lens)
     top = max(max(lens), 1)
+    _, mps, mnp = plan(lib, len(lens), hkv, top)
     assert st == OK
     assert ps > 0 and ps % 16 == 0 and ps * npart >= top
-    if npart > 1:
-        assert ps % 32 == 0 and ps >= 128
+    if (ps, npart) != (mps, mnp):
+        # taken from the lengths: at most one live workgroup per CU, the
+        # smallest such partition, and at most 2/3 of the longest-based one
+        assert npart > 1 and ps % 32 == 0 and ps >= 128
         assert ps * (npart - 1) < top
         assert _live(hkv, lens, ps) <= 256
-        assert ps == 128 or _live(hkv, lens, ps - 32) > 256   # the smallest such size
+        assert ps == 128 or _live(hkv, lens, ps - 32) > 256
+        assert 3 * ps <= 2 * mps
 
 
 def test_split_plan_lens_validation(lib):

@@ -195,16 +195,17 @@ def test_negative_context_gives_nan_in_every_plan(ps, P):
 
 
 def test_decode_mixed_lengths_plan_parity():
-    """The hybrid batch (4097- and 8192-token contexts, 2 KV heads) in the
-    plan made from its actual lengths (20 partitions of 416 tokens: 240 live
-    workgroups instead of 200 with the maximum-based 16 x 512), at the
-    literal bar."""
-    announce("decode hybrid_decode_b8, plan from lengths")
-    case = workloads.hybrid_decode()
+    """One 8192-token request among seven of ~1100 tokens (Qwen3-32B heads)
+    in the plan made from the batch's lengths: 15 partitions of 576 tokens
+    (232 live workgroups of 960, ranked first) instead of 4 x 2048 from the
+    longest alone; at the literal bar."""
+    announce("decode qwen3_32b_decode_mixed_b8, plan from lengths")
+    case = workloads.qwen3_32b_decode_mixed()
     ps, P = pa.decode_split_plan_lens(case.num_kv_heads, case.context_lens)
-    assert (ps, P) == (416, 20)
+    assert (ps, P) == (576, 15)
+    assert pa.decode_split_plan(case.batch, case.num_kv_heads, 8192, 256) == (2048, 4)
     out = decode_gpu(case, partition_size=ps, num_partitions=P)
-    check_tolerance("hybrid decode, plan from lengths", out, decode_oracle(case), literal=True)
+    check_tolerance("mixed batch, plan from lengths", out, decode_oracle(case), literal=True)
 
 
 def test_block_permutation_and_contiguous_twin_bitwise_split_plan_from_lengths():
@@ -221,3 +222,45 @@ def test_block_permutation_and_contiguous_twin_bitwise_split_plan_from_lengths()
     assert torch.equal(decode_gpu(contiguous_twin(case), partition_size=ps,
                                   num_partitions=P).view(torch.int16), base.view(torch.int16))
     check_tolerance("mixed lengths", base, decode_oracle(case), literal=True)
+
+
+@pytest.mark.parametrize("hkv,d,lens", [
+    (2, 256, [4097, 300, 8192, 17, 0, 1000, 4097, 129]),
+    (8, 128, [8192, 100, 100, 100]),                    # one long request among short ones
+    (4, 64, [1, 2000, 33, 2000, 700, 64])])
+def test_decode_partials_mixed_lengths_every_piece(hkv, d, lens):
+    """In a mixed batch the launch ranks the (sequence, partition) pairs
+    that hold keys first and the empty ones last; every piece must still be
+    written exactly once: each partial output and LSE against the oracle's,
+    empty partitions included (0 and -inf), then the reduce."""
+    announce(f"decode partials mixed lengths hkv={hkv} d={d}")
+    hq = 8 * hkv
+    case = workloads.make_decode_case("mixparts", context_lens=lens, num_q_heads=hq,
+                                      num_kv_heads=hkv, head_dim=d,
+                                      num_blocks=sum(-(-c // 16) for c in lens) + 4,
+                                      sigma=0.5, seed=hkv * 10 + d)
+    ps, P = pa.decode_split_plan_lens(hkv, case.context_lens)
+    assert P > 1
+    kc, vc = case.k_cache.to(DEV), case.v_cache.to(DEV)
+    pa.write_kv(case.k_new.to(DEV), case.v_new.to(DEV), case.slot_mapping.to(DEV), kc, vc)
+    po = torch.full((len(lens), hq, P, d), float("nan"), device=DEV)   # unwritten stays NaN
+    pl = torch.full((len(lens), hq, P), float("nan"), device=DEV)
+    pa.decode_partials(case.q.to(DEV), kc, vc, case.block_tables.to(DEV),
+                       case.context_lens.to(DEV), case.scale, ps, P, part_out=po, part_lse=pl)
+    torch.cuda.synchronize()
+    okc, ovc = oracle.write_kv(bits(case.k_cache), bits(case.v_cache), bits(case.k_new),
+                               bits(case.v_new), case.slot_mapping.numpy())
+    rpo, rpl = oracle.decode_partials(bits(case.q), okc, ovc, case.block_tables.numpy(),
+                                      case.context_lens.numpy(), case.scale, hq, hkv, ps, P)
+    gpo, gpl = po.cpu().double().numpy(), pl.cpu().double().numpy()
+    assert np.isfinite(gpo).all()
+    empty = np.isneginf(rpl)
+    assert np.array_equal(np.isneginf(gpl), empty)
+    assert np.abs(gpl[~empty] - rpl[~empty]).max() < 1e-3
+    assert (gpo[empty] == 0).all()
+    err = np.abs(gpo - rpo)
+    assert err.max() < 4e-3 and err.mean() < 5e-4, (err.max(), err.mean())
+    out = pa.decode_reduce(po, pl, case.context_lens.to(DEV), ps)
+    torch.cuda.synchronize()
+    check_tolerance(f"mixed reduce hkv={hkv} d={d}", out.cpu(), decode_oracle(case),
+                    literal=True)

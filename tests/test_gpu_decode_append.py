@@ -117,12 +117,14 @@ def test_decode_append_negative_context(ps, P):
 
 
 def test_decode_append_mixed_lengths_plan_parity():
-    """The hybrid batch appended and decoded in the plan made from its
-    lengths (20 x 416), literal bar; pools bit-exact."""
-    announce("decode_append hybrid_decode_b8, plan from lengths")
-    case = workloads.hybrid_decode()
+    """The mixed batch (one 8192-token request among seven of ~1100 tokens)
+    appended and decoded in the plan made from its lengths (15 x 576, items
+    ranked live first), literal bar; pools bit-exact."""
+    announce("decode_append qwen3_32b_decode_mixed_b8, plan from lengths")
+    case = workloads.qwen3_32b_decode_mixed()
     ps, P = pa.decode_split_plan_lens(case.num_kv_heads, case.context_lens)
     out, kc, vc = _append_gpu(case, ps, P)
-    check_tolerance("append hybrid, plan from lengths", out, decode_oracle(case), literal=True)
+    check_tolerance("append mixed batch, plan from lengths", out, decode_oracle(case),
+                    literal=True)
     okc, ovc = _oracle_pools(case)
     assert np.array_equal(bits(kc), okc) and np.array_equal(bits(vc), ovc)

@@ -346,6 +346,18 @@ def qwen3_32b_decode_long(seed=42, poison=True):
                             seed=seed, poison=poison)
 
 
+def qwen3_32b_decode_mixed(seed=42, poison=True):
+    """One 8192-token request decoding among seven ordinary ones (contexts
+    U{1024..1152}), Qwen3-32B heads: a batch of mixed lengths as continuous
+    batching produces it (the long-prompt lengths of "Qwen3.5-4B / 9B /
+    27B" beside the 1024-token serving prompts)."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    lens = [8192] + torch.randint(1024, 1153, (7,), generator=g).tolist()
+    return make_decode_case("qwen3_32b_decode_mixed_b8", context_lens=lens, num_q_heads=64,
+                            num_kv_heads=8, head_dim=128, num_blocks=2048, seed=seed,
+                            poison=poison)
+
+
 def hybrid_decode(seed=42, poison=True):
     """Full-attention layer of a hybrid model: 16/2 heads, head_dim 256, sigma 0.5,
     batch 8 with contexts 4097 and 8192 interleaved."""
