@@ -191,6 +191,27 @@ __device__ __forceinline__ void patch_pair(PairRegs<D>& r, const u32x4 (&newk)[D
   }
 }
 
+// Writes the appended token's K row pieces and V values, as lane (col, c)
+// holds them (see patch_pair), into the pools at offset `off` of KV tile
+// `tile` (= block * Hkv + KV head): lanes with col == 0 store the K pieces,
+// lanes with c == 0 the V values.
+template <int D>
+__device__ __forceinline__ void store_new_row(uint16_t* k_pool, uint16_t* v_pool,
+                                              const u32x4 (&newk)[D / 32],
+                                              const uint32_t (&newv)[D / 16], int64_t tile,
+                                              int off, int col, int c) {
+  if (col == 0) {
+    uint16_t* kd = k_pool + (tile * kBlock + off) * D + 8 * c;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) *reinterpret_cast<u32x4*>(kd + 32 * i) = newk[i];
+  }
+  if (c == 0) {
+    uint16_t* vd = v_pool + (tile * D + col) * kBlock + off;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) vd[16 * dt * kBlock] = (uint16_t)newv[dt];
+  }
+}
+
 // Query tokens per sequence: query_len; columns per KV head: query_len *
 // group, taken NT tiles of 16 at a time by `num_chunks` workgroups.  The
 // chunks of one (partition, KV head, sequence) read the same K/V, so they
@@ -202,9 +223,14 @@ __device__ __forceinline__ void patch_pair(PairRegs<D>& r, const u32x4 (&newk)[D
 // K/V (k_new/v_new [B, Hkv, D]) at position ctx-1 through the block table.
 // Every lane holds its slice of the new row from the start; the pair that
 // covers position ctx-1 takes those values instead of the pool's (which may
-// or may not have been written yet), and wave 0 of the workgroup whose
-// partition holds ctx-1 writes the row into the pools.  k_pool/v_pool are
-// the same pools as k_cache/v_cache; no reader depends on those stores.
+// or may not have been written yet), and the wave that owns that pair writes
+// the row into the pools.  k_pool/v_pool are the same pools as
+// k_cache/v_cache; no reader depends on those stores.  The block number comes
+// from the table entries the wave loads for its own pairs.  Up to head_dim
+// 128 the row is stored after the wave's last pair: a store issued ahead of
+// the pair loads delays them (one-partition batches take ~2% longer).  At
+// head_dim 256 the row's registers cannot stay live past the loop without
+// spilling, so the row is stored before the loads.
 //
 // COMPACT (split launches of up to 64 sequences that need more than one
 // dispatch round): items are ranked so that those holding keys come first
@@ -338,6 +364,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
   // The appended token: this lane's pieces of its K row (the d-slices its
   // pool K loads cover) and its V values at d = 16*dt + col.
   const int pos_new = ctx - 1;
+  constexpr bool kStoreLate = D <= 128;
   u32x4 newk[APPEND ? KS : 1];
   uint32_t newv[APPEND ? DT : 1];
   if constexpr (APPEND) {
@@ -346,31 +373,21 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
     for (int i = 0; i < KS; ++i) newk[i] = load16(k_new + src + 8 * c + 32 * i);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) newv[dt] = v_new[src + 16 * dt + col];
-    // Wave 0 of the workgroup whose partition holds ctx-1 stores the row
-    // (lanes with col == 0 the K pieces, lanes with c == 0 the V values).
-    if (wave == 0 && chunk == 0 && ctx > 0 && !bad && pos_new / kBlock >= pb0 &&
-        pos_new / kBlock < pb0 + blocks_per_part) {
-      const int64_t blk = bt[pos_new / kBlock];
-      if (blk >= 0 && blk < num_blocks) {
-        const int64_t tile = blk * num_kv_heads + g;
-        const int off = pos_new % kBlock;
-        if (col == 0) {
-          uint16_t* kd = k_pool + (tile * kBlock + off) * D + 8 * c;
-#pragma unroll
-          for (int i = 0; i < KS; ++i) *reinterpret_cast<u32x4*>(kd + 32 * i) = newk[i];
-        }
-        if (c == 0) {
-          uint16_t* vd = v_pool + (tile * D + col) * kBlock + off;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) vd[16 * dt * kBlock] = (uint16_t)newv[dt];
-        }
-      }
+    // Early store (head_dim 256): position ctx-1's table entry is one of the
+    // 64 the wave has loaded, unless its range is longer than 32 pairs.
+    const int nb = pos_new / kBlock - wb0;  // wave-uniform
+    if (!kStoreLate && chunk == 0 && ctx > 0 && nb >= 0 && nb < 2 * nk) {
+      const int64_t blk = nb < 64 ? __builtin_amdgcn_readlane(ent, nb) : bt[wb0 + nb];
+      if (blk >= 0 && blk < num_blocks)
+        store_new_row<D>(k_pool, v_pool, newk, newv, blk * num_kv_heads + g, pos_new % kBlock,
+                         col, c);
     }
   }
 
   // Issue the loads of this wave's pair k into `r`.  An entry outside the
   // pool marks the sequence bad (NaN output) and is replaced by block 0 so
   // the loads stay in bounds (num_blocks == 0 never gets here: see above).
+  int64_t new_blk = -1;  // late store: pool block of position ctx-1, if this wave has it
   auto issue = [&](int k, PairRegs<D>& r) {
     if ((k & 31) == 0 && k > 0) load_entries(k >> 5);
     const int e = 2 * (k & 31);
@@ -380,6 +397,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
     const bool okx = px >= 0 && px < num_blocks;
     const bool oky = py >= 0 && py < num_blocks;
     bad |= !okx || (hy && !oky);
+    if constexpr (APPEND && kStoreLate) {
+      const int rel = pos_new - (wb0 + 2 * k) * kBlock;  // wave-uniform
+      if (rel >= 0 && rel < 2 * kBlock) new_blk = rel < kBlock ? (okx ? px : -1) : (oky ? py : -1);
+    }
     px = okx ? px : 0;
     py = (hy && oky) ? py : px;
     load_pair<D>(r, k_cache, v_cache, px, py, g, num_kv_heads, col, c);
@@ -405,6 +426,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
         if (k + NBUF < nk) issue(k + NBUF, buf[b]);
       }
     }
+  }
+
+  if constexpr (APPEND && kStoreLate) {
+    if (chunk == 0 && new_blk >= 0)
+      store_new_row<D>(k_pool, v_pool, newk, newv, new_blk * num_kv_heads + g, pos_new % kBlock,
+                       col, c);
   }
 
   // Per-wave totals: l over the four lane groups of each column.
@@ -628,17 +655,29 @@ int launch_decode(void* out, float* part_out, float* part_lse, const void* q,
   // exactly 3 pairs (two-tile form, Qwen3-4B verify batch 8: 13.8 -> 13.1 us,
   // 12.8 with 2 pairs in flight).  The plain form keeps 2 pairs in flight
   // per wave (Qwen3-4B batch 8: 11.4 -> 10.1 us against 4 waves with 1 pair
-  // in flight); the appending form keeps 1 (11.2 -> 10.8 us; with 2 its
-  // register patching makes the compiler wait for both pairs).
+  // in flight); the appending form keeps 1 (11.2 -> 10.8 us; with 2 it needs
+  // 288 registers, one wave per SIMD).  Once partitions hold 32 pairs or
+  // more, both single-tile forms take 4 waves: the tail imbalance is small
+  // there and the extra wave's loads in flight pay (appending, Qwen3-32B
+  // batch 64 at 36 pairs: 52.0 -> 51.2 us, batch 4 x 8192 at 32: 25.5 ->
+  // 25.1; plain, batch 64: 49.8 -> 49.1, 16 x 8192 in 2 x 4096: 87.3 ->
+  // 85.5).  The two forms split partitions alike, so they give bit-identical
+  // results.
   auto pick = [&](auto compact_tag) {
     constexpr bool C = decltype(compact_tag)::value;
     switch (head_dim * 8 + nt * 2 + (append ? 1 : 0)) {
       case 64 * 8 + 2: go(decode_kernel<64, 4, 4, 1, false, C>, 4); return 0;
       case 64 * 8 + 4: go(decode_kernel<64, 4, 4, 2, false, C>, 4); return 0;
       case 64 * 8 + 3: go(decode_kernel<64, 4, 4, 1, true, C>, 4); return 0;
-      case 128 * 8 + 2: go(decode_kernel<128, 3, 2, 1, false, C>, 3); return 0;
+      case 128 * 8 + 2:
+        if (bpp >= 64) go(decode_kernel<128, 4, 2, 1, false, C>, 4);
+        else go(decode_kernel<128, 3, 2, 1, false, C>, 3);
+        return 0;
       case 128 * 8 + 4: go(decode_kernel<128, 3, 2, 2, false, C>, 3); return 0;
-      case 128 * 8 + 3: go(decode_kernel<128, 3, 1, 1, true, C>, 3); return 0;
+      case 128 * 8 + 3:
+        if (bpp >= 64) go(decode_kernel<128, 4, 1, 1, true, C>, 4);
+        else go(decode_kernel<128, 3, 1, 1, true, C>, 3);
+        return 0;
       case 256 * 8 + 2: go(decode_kernel<256, 4, 2, 1, false, C>, 4); return 0;
       case 256 * 8 + 4: go(decode_kernel<256, 4, 1, 2, false, C>, 4); return 0;
       case 256 * 8 + 3: go(decode_kernel<256, 4, 2, 1, true, C>, 4); return 0;

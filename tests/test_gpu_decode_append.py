@@ -72,6 +72,28 @@ def test_decode_append_new_token_positions(hq, hkv, d):
         assert np.array_equal(bits(kc), ek) and np.array_equal(bits(vc), ev)
 
 
+@pytest.mark.parametrize("hq,hkv,d", [(8, 2, 64), (16, 2, 128), (16, 2, 256)])
+def test_decode_append_long_wave_ranges(hq, hkv, d):
+    """One partition of 8192 tokens, so every wave's range holds 64 pairs:
+    the waves reload their table entries after 32 pairs, and the new token
+    lies at the start of a wave's range (ctx 4097, 2050, 1), within its first
+    64 entries (5000) and past them (8192; at head_dim 256, whose row is
+    stored before the loads, that entry is read from the table).  Pools
+    bit-exact, output against the oracle and bit-identical to pa_write_kv +
+    pa_decode."""
+    announce(f"decode_append long wave ranges hq={hq} hkv={hkv} d={d}")
+    lens = [8192, 5000, 4097, 2050, 1]
+    case = workloads.make_decode_case("longwave", context_lens=lens, num_q_heads=hq,
+                                      num_kv_heads=hkv, head_dim=d, num_blocks=1300,
+                                      seed=d + 7)
+    ref = decode_oracle(case)
+    ek, ev = _oracle_pools(case)
+    out, kc, vc = _append_gpu(case, partition_size=8192, num_partitions=1)
+    check_tolerance(f"long wave ranges d={d}", out, ref)
+    assert np.array_equal(bits(kc), ek) and np.array_equal(bits(vc), ev)
+    assert torch.equal(out, decode_gpu(case, partition_size=8192))
+
+
 def test_decode_append_bad_entry_poisons_and_skips_write():
     """A table entry outside the pool for the new token's block: NaN outputs
     for that sequence and nothing written for it; the other sequence's token
