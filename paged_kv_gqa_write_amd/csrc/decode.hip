@@ -212,6 +212,52 @@ __device__ __forceinline__ void store_new_row(uint16_t* k_pool, uint16_t* v_pool
   }
 }
 
+// As patch_pair and store_new_row, with the new token's K and V rows read
+// from this wave's LDS copy (kr, vr: D elements each) instead of registers.
+template <int D>
+__device__ __forceinline__ void patch_pair_lds(PairRegs<D>& r, const uint16_t* kr,
+                                               const uint16_t* vr, int rel, int col, int c,
+                                               int lane_key0) {
+  const int gr = col >> 2;
+  const int krow = ((gr >= 2) ? kBlock : 0) + 8 * (gr & 1) + (col & 3);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+    if (krow + 4 * t == rel) {
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) r.k[t][i] = *reinterpret_cast<const u32x4*>(kr + 8 * c + 32 * i);
+    }
+  const int e = rel - lane_key0;
+  if (e >= 0 && e < 8) {
+    const int w = e >> 1;
+    const uint32_t keep = (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+    const int sh = (e & 1) ? 16 : 0;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const uint32_t nv = vr[16 * dt + col];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (q == w) r.v[dt][q] = (r.v[dt][q] & keep) | (nv << sh);
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_new_row_lds(uint16_t* k_pool, uint16_t* v_pool,
+                                                  const uint16_t* kr, const uint16_t* vr,
+                                                  int64_t tile, int off, int col, int c) {
+  if (col == 0) {
+    uint16_t* kd = k_pool + (tile * kBlock + off) * D + 8 * c;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+      *reinterpret_cast<u32x4*>(kd + 32 * i) = *reinterpret_cast<const u32x4*>(kr + 8 * c + 32 * i);
+  }
+  if (c == 0) {
+    uint16_t* vd = v_pool + (tile * D + col) * kBlock + off;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) vd[16 * dt * kBlock] = vr[16 * dt + col];
+  }
+}
+
 // Query tokens per sequence: query_len; columns per KV head: query_len *
 // group, taken NT tiles of 16 at a time by `num_chunks` workgroups.  The
 // chunks of one (partition, KV head, sequence) read the same K/V, so they
@@ -226,11 +272,18 @@ __device__ __forceinline__ void store_new_row(uint16_t* k_pool, uint16_t* v_pool
 // or may not have been written yet), and the wave that owns that pair writes
 // the row into the pools.  k_pool/v_pool are the same pools as
 // k_cache/v_cache; no reader depends on those stores.  The block number comes
-// from the table entries the wave loads for its own pairs.  Up to head_dim
-// 128 the row is stored after the wave's last pair: a store issued ahead of
-// the pair loads delays them (one-partition batches take ~2% longer).  At
-// head_dim 256 the row's registers cannot stay live past the loop without
-// spilling, so the row is stored before the loads.
+// from the table entries the wave loads for its own pairs (a pair whose second
+// block lies past the partition does not own a token in that block).  Position
+// ctx-1 is the last key, so its pair is the last one the owning wave loads: up
+// to head_dim 128 the row is stored right behind that pair's loads, where no
+// later wait of the wave depends on the store and its latency overlaps the
+// pair's own (a store ahead of other pair loads delays them; one at the very
+// end delays the launch's completion).  At head_dim 256 the row is stored
+// before the loads (a store later in the loop spills registers there).  With
+// two or more pairs in flight (head_dim <= 128) the row would not fit in
+// registers beside the ring, so each wave copies it into its own LDS slot
+// right after its first loads and reads it from there for the patch and the
+// store.
 //
 // COMPACT (split launches of up to 64 sequences that need more than one
 // dispatch round): items are ranked so that those holding keys come first
@@ -243,7 +296,7 @@ __device__ __forceinline__ void store_new_row(uint16_t* k_pool, uint16_t* v_pool
 // partition), as its empty ones do.  When every sequence fills every
 // partition this is the plain order.
 template <int D, int NW, int NBUF, int NT, bool APPEND, bool COMPACT>
-__global__ __launch_bounds__(NW * 64) void decode_kernel(
+__global__ __launch_bounds__(NW * 64, (APPEND && NBUF >= 2 && D <= 128) ? 2 : 1) void decode_kernel(
     uint16_t* __restrict__ out, float* __restrict__ part_out, float* __restrict__ part_lse,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
@@ -365,9 +418,21 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
   // pool K loads cover) and its V values at d = 16*dt + col.
   const int pos_new = ctx - 1;
   constexpr bool kStoreLate = D <= 128;
-  u32x4 newk[APPEND ? KS : 1];
-  uint32_t newv[APPEND ? DT : 1];
-  if constexpr (APPEND) {
+  // With two or more pairs in flight the row does not fit in registers next
+  // to the ring: each wave keeps it in its own LDS slot instead.
+  constexpr bool kRowLds = APPEND && kStoreLate && NBUF >= 2;
+  u32x4 newk[APPEND && !kRowLds ? KS : 1];
+  uint32_t newv[APPEND && !kRowLds ? DT : 1];
+  __shared__ __attribute__((aligned(16))) uint16_t sm_new[kRowLds ? NW : 1][2][D];
+  uint32_t nkw = 0, nvw = 0;
+  if constexpr (kRowLds) {
+    const int64_t src = ((int64_t)s * num_kv_heads + g) * D;
+    if (2 * lane < D) {
+      nkw = *reinterpret_cast<const uint32_t*>(k_new + src + 2 * lane);
+      nvw = *reinterpret_cast<const uint32_t*>(v_new + src + 2 * lane);
+    }
+  }
+  if constexpr (APPEND && !kRowLds) {
     const int64_t src = ((int64_t)s * num_kv_heads + g) * D;
 #pragma unroll
     for (int i = 0; i < KS; ++i) newk[i] = load16(k_new + src + 8 * c + 32 * i);
@@ -376,7 +441,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
     // Early store (head_dim 256): position ctx-1's table entry is one of the
     // 64 the wave has loaded, unless its range is longer than 32 pairs.
     const int nb = pos_new / kBlock - wb0;  // wave-uniform
-    if (!kStoreLate && chunk == 0 && ctx > 0 && nb >= 0 && nb < 2 * nk) {
+    if (!kStoreLate && chunk == 0 && ctx > 0 && nb >= 0 && nb < 2 * nk && wb0 + nb < pb1) {
       const int64_t blk = nb < 64 ? __builtin_amdgcn_readlane(ent, nb) : bt[wb0 + nb];
       if (blk >= 0 && blk < num_blocks)
         store_new_row<D>(k_pool, v_pool, newk, newv, blk * num_kv_heads + g, pos_new % kBlock,
@@ -387,7 +452,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
   // Issue the loads of this wave's pair k into `r`.  An entry outside the
   // pool marks the sequence bad (NaN output) and is replaced by block 0 so
   // the loads stay in bounds (num_blocks == 0 never gets here: see above).
-  int64_t new_blk = -1;  // late store: pool block of position ctx-1, if this wave has it
+  int64_t pend_blk = -1;
+  auto store_pending = [&]() {
+    if constexpr (kRowLds) {
+      if (pend_blk >= 0) {
+        store_new_row_lds<D>(k_pool, v_pool, sm_new[wave][0], sm_new[wave][1],
+                             pend_blk * num_kv_heads + g, pos_new % kBlock, col, c);
+        pend_blk = -1;
+      }
+    }
+  };
   auto issue = [&](int k, PairRegs<D>& r) {
     if ((k & 31) == 0 && k > 0) load_entries(k >> 5);
     const int e = 2 * (k & 31);
@@ -397,13 +471,27 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
     const bool okx = px >= 0 && px < num_blocks;
     const bool oky = py >= 0 && py < num_blocks;
     bad |= !okx || (hy && !oky);
+    int64_t store_blk = -1;
     if constexpr (APPEND && kStoreLate) {
       const int rel = pos_new - (wb0 + 2 * k) * kBlock;  // wave-uniform
-      if (rel >= 0 && rel < 2 * kBlock) new_blk = rel < kBlock ? (okx ? px : -1) : (oky ? py : -1);
+      if (rel >= 0 && rel < kBlock) store_blk = okx ? px : -1;
+      else if (rel >= kBlock && rel < 2 * kBlock && hy) store_blk = oky ? py : -1;
     }
     px = okx ? px : 0;
     py = (hy && oky) ? py : px;
     load_pair<D>(r, k_cache, v_cache, px, py, g, num_kv_heads, col, c);
+    // The pair holding position ctx-1 is the last one this wave loads: the
+    // row goes out right behind its loads, so no wait of the wave follows it
+    // (from LDS, right after the row is there when the pair is in the prologue).
+    if constexpr (APPEND && kStoreLate) {
+      if (chunk == 0 && store_blk >= 0) {
+        if constexpr (kRowLds)
+          pend_blk = store_blk;
+        else
+          store_new_row<D>(k_pool, v_pool, newk, newv, store_blk * num_kv_heads + g,
+                           pos_new % kBlock, col, c);
+      }
+    }
   };
 
   // Ring of NBUF register buffers: NBUF pairs are in flight while one is
@@ -412,6 +500,13 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
 #pragma unroll
   for (int b = 0; b < NBUF; ++b)
     if (b < nk) issue(b, buf[b]);
+  if constexpr (kRowLds) {
+    if (2 * lane < D) {
+      *reinterpret_cast<uint32_t*>(&sm_new[wave][0][2 * lane]) = nkw;
+      *reinterpret_cast<uint32_t*>(&sm_new[wave][1][2 * lane]) = nvw;
+    }
+    store_pending();
+  }
   for (int kb = 0; kb < nk; kb += NBUF) {
 #pragma unroll
     for (int b = 0; b < NBUF; ++b) {
@@ -419,20 +514,23 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(
       if (k < nk) {
         if constexpr (APPEND) {
           const int rel = pos_new - (wb0 + 2 * k) * kBlock;  // wave-uniform
-          if (rel >= 0 && rel < 2 * kBlock) patch_pair<D>(buf[b], newk, newv, rel, col, lane_key0);
+          if (rel >= 0 && rel < 2 * kBlock) {
+            if constexpr (kRowLds)
+              patch_pair_lds<D>(buf[b], sm_new[wave][0], sm_new[wave][1], rel, col, c, lane_key0);
+            else
+              patch_pair<D>(buf[b], newk, newv, rel, col, lane_key0);
+          }
         }
         compute_pair<D, NT>(buf[b], qf, acc, m_run, l_run, (wb0 + 2 * k) * kBlock + lane_key0,
                             limit, climit, scale_log2);
-        if (k + NBUF < nk) issue(k + NBUF, buf[b]);
+        if (k + NBUF < nk) {
+          issue(k + NBUF, buf[b]);
+          store_pending();
+        }
       }
     }
   }
 
-  if constexpr (APPEND && kStoreLate) {
-    if (chunk == 0 && new_blk >= 0)
-      store_new_row<D>(k_pool, v_pool, newk, newv, new_blk * num_kv_heads + g, pos_new % kBlock,
-                       col, c);
-  }
 
   // Per-wave totals: l over the four lane groups of each column.
 #pragma unroll
@@ -655,9 +753,11 @@ int launch_decode(void* out, float* part_out, float* part_lse, const void* q,
   // exactly 3 pairs (two-tile form, Qwen3-4B verify batch 8: 13.8 -> 13.1 us,
   // 12.8 with 2 pairs in flight).  The plain form keeps 2 pairs in flight
   // per wave (Qwen3-4B batch 8: 11.4 -> 10.1 us against 4 waves with 1 pair
-  // in flight); the appending form keeps 1 (11.2 -> 10.8 us; with 2 it needs
-  // 288 registers, one wave per SIMD).  Once partitions hold 32 pairs or
-  // more, both single-tile forms take 4 waves: the tail imbalance is small
+  // in flight); the appending form keeps 2 as well, its new row in LDS
+  // (10.6 -> 10.35 us; with the row in registers 2 pairs need 288 registers,
+  // one wave per SIMD).  Once partitions hold 32 pairs or more, both
+  // single-tile forms take 4 waves (the appending one with 1 pair in flight,
+  // its row in registers: 50.6 against 50.9 us): the tail imbalance is small
   // there and the extra wave's loads in flight pay (appending, Qwen3-32B
   // batch 64 at 36 pairs: 52.0 -> 51.2 us, batch 4 x 8192 at 32: 25.5 ->
   // 25.1; plain, batch 64: 49.8 -> 49.1, 16 x 8192 in 2 x 4096: 87.3 ->
@@ -676,7 +776,7 @@ int launch_decode(void* out, float* part_out, float* part_lse, const void* q,
       case 128 * 8 + 4: go(decode_kernel<128, 3, 2, 2, false, C>, 3); return 0;
       case 128 * 8 + 3:
         if (bpp >= 64) go(decode_kernel<128, 4, 1, 1, true, C>, 4);
-        else go(decode_kernel<128, 3, 1, 1, true, C>, 3);
+        else go(decode_kernel<128, 3, 2, 1, true, C>, 3);
         return 0;
       case 256 * 8 + 2: go(decode_kernel<256, 4, 2, 1, false, C>, 4); return 0;
       case 256 * 8 + 4: go(decode_kernel<256, 4, 1, 2, false, C>, 4); return 0;
