@@ -274,16 +274,14 @@ __device__ __forceinline__ void store_new_row_lds(uint16_t* k_pool, uint16_t* v_
 // k_cache/v_cache; no reader depends on those stores.  The block number comes
 // from the table entries the wave loads for its own pairs (a pair whose second
 // block lies past the partition does not own a token in that block).  Position
-// ctx-1 is the last key, so its pair is the last one the owning wave loads: up
-// to head_dim 128 the row is stored right behind that pair's loads, where no
-// later wait of the wave depends on the store and its latency overlaps the
-// pair's own (a store ahead of other pair loads delays them; one at the very
-// end delays the launch's completion).  At head_dim 256 the row is stored
-// before the loads (a store later in the loop spills registers there).  With
-// two or more pairs in flight (head_dim <= 128) the row would not fit in
-// registers beside the ring, so each wave copies it into its own LDS slot
-// right after its first loads and reads it from there for the patch and the
-// store.
+// ctx-1 is the last key, so its pair is the last one the owning wave loads:
+// the row is stored right behind that pair's loads, where no later wait of
+// the wave depends on the store and its latency overlaps the pair's own (a
+// store ahead of other pair loads delays them; one at the very end delays the
+// launch's completion).  With two or more pairs in flight the row would not
+// fit in registers beside the ring, so each wave copies it into its own LDS
+// slot right after its first loads and reads it from there for the patch and
+// the store.
 //
 // COMPACT (split launches of up to 64 sequences that need more than one
 // dispatch round): items are ranked so that those holding keys come first
@@ -417,19 +415,23 @@ __global__ __launch_bounds__(NW * 64, (APPEND && NBUF >= 2 && D <= 128) ? 2 : 1)
   // The appended token: this lane's pieces of its K row (the d-slices its
   // pool K loads cover) and its V values at d = 16*dt + col.
   const int pos_new = ctx - 1;
-  constexpr bool kStoreLate = D <= 128;
   // With two or more pairs in flight the row does not fit in registers next
   // to the ring: each wave keeps it in its own LDS slot instead.
-  constexpr bool kRowLds = APPEND && kStoreLate && NBUF >= 2;
+  constexpr bool kRowLds = APPEND && NBUF >= 2;
   u32x4 newk[APPEND && !kRowLds ? KS : 1];
   uint32_t newv[APPEND && !kRowLds ? DT : 1];
   __shared__ __attribute__((aligned(16))) uint16_t sm_new[kRowLds ? NW : 1][2][D];
-  uint32_t nkw = 0, nvw = 0;
+  constexpr int kRowWords = (D + 127) / 128;  // 2-element words per lane
+  uint32_t nkw[kRowWords], nvw[kRowWords];
   if constexpr (kRowLds) {
     const int64_t src = ((int64_t)s * num_kv_heads + g) * D;
-    if (2 * lane < D) {
-      nkw = *reinterpret_cast<const uint32_t*>(k_new + src + 2 * lane);
-      nvw = *reinterpret_cast<const uint32_t*>(v_new + src + 2 * lane);
+#pragma unroll
+    for (int w = 0; w < kRowWords; ++w) {
+      const int o = 2 * lane + 128 * w;
+      if (o < D) {
+        nkw[w] = *reinterpret_cast<const uint32_t*>(k_new + src + o);
+        nvw[w] = *reinterpret_cast<const uint32_t*>(v_new + src + o);
+      }
     }
   }
   if constexpr (APPEND && !kRowLds) {
@@ -438,15 +440,6 @@ __global__ __launch_bounds__(NW * 64, (APPEND && NBUF >= 2 && D <= 128) ? 2 : 1)
     for (int i = 0; i < KS; ++i) newk[i] = load16(k_new + src + 8 * c + 32 * i);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) newv[dt] = v_new[src + 16 * dt + col];
-    // Early store (head_dim 256): position ctx-1's table entry is one of the
-    // 64 the wave has loaded, unless its range is longer than 32 pairs.
-    const int nb = pos_new / kBlock - wb0;  // wave-uniform
-    if (!kStoreLate && chunk == 0 && ctx > 0 && nb >= 0 && nb < 2 * nk && wb0 + nb < pb1) {
-      const int64_t blk = nb < 64 ? __builtin_amdgcn_readlane(ent, nb) : bt[wb0 + nb];
-      if (blk >= 0 && blk < num_blocks)
-        store_new_row<D>(k_pool, v_pool, newk, newv, blk * num_kv_heads + g, pos_new % kBlock,
-                         col, c);
-    }
   }
 
   // Issue the loads of this wave's pair k into `r`.  An entry outside the
@@ -472,7 +465,7 @@ __global__ __launch_bounds__(NW * 64, (APPEND && NBUF >= 2 && D <= 128) ? 2 : 1)
     const bool oky = py >= 0 && py < num_blocks;
     bad |= !okx || (hy && !oky);
     int64_t store_blk = -1;
-    if constexpr (APPEND && kStoreLate) {
+    if constexpr (APPEND) {
       const int rel = pos_new - (wb0 + 2 * k) * kBlock;  // wave-uniform
       if (rel >= 0 && rel < kBlock) store_blk = okx ? px : -1;
       else if (rel >= kBlock && rel < 2 * kBlock && hy) store_blk = oky ? py : -1;
@@ -483,7 +476,7 @@ __global__ __launch_bounds__(NW * 64, (APPEND && NBUF >= 2 && D <= 128) ? 2 : 1)
     // The pair holding position ctx-1 is the last one this wave loads: the
     // row goes out right behind its loads, so no wait of the wave follows it
     // (from LDS, right after the row is there when the pair is in the prologue).
-    if constexpr (APPEND && kStoreLate) {
+    if constexpr (APPEND) {
       if (chunk == 0 && store_blk >= 0) {
         if constexpr (kRowLds)
           pend_blk = store_blk;
@@ -501,9 +494,13 @@ __global__ __launch_bounds__(NW * 64, (APPEND && NBUF >= 2 && D <= 128) ? 2 : 1)
   for (int b = 0; b < NBUF; ++b)
     if (b < nk) issue(b, buf[b]);
   if constexpr (kRowLds) {
-    if (2 * lane < D) {
-      *reinterpret_cast<uint32_t*>(&sm_new[wave][0][2 * lane]) = nkw;
-      *reinterpret_cast<uint32_t*>(&sm_new[wave][1][2 * lane]) = nvw;
+#pragma unroll
+    for (int w = 0; w < kRowWords; ++w) {
+      const int o = 2 * lane + 128 * w;
+      if (o < D) {
+        *reinterpret_cast<uint32_t*>(&sm_new[wave][0][o]) = nkw[w];
+        *reinterpret_cast<uint32_t*>(&sm_new[wave][1][o]) = nvw[w];
+      }
     }
     store_pending();
   }
