@@ -267,9 +267,9 @@ __device__ __forceinline__ void store_new_row_lds(uint16_t* k_pool, uint16_t* v_
 //
 // APPEND (one query token per sequence): the kernel also appends the token's
 // K/V (k_new/v_new [B, Hkv, D]) at position ctx-1 through the block table.
-// Every lane holds its slice of the new row from the start; the pair that
-// covers position ctx-1 takes those values instead of the pool's (which may
-// or may not have been written yet), and the wave that owns that pair writes
+// The new row is loaded at the start; in the pair that covers position ctx-1
+// the lanes take its values instead of the pool's (which may or may not have
+// been written yet), and the wave that owns that pair writes
 // the row into the pools.  k_pool/v_pool are the same pools as
 // k_cache/v_cache; no reader depends on those stores.  The block number comes
 // from the table entries the wave loads for its own pairs (a pair whose second
@@ -412,8 +412,8 @@ __global__ __launch_bounds__(NW * 64, (APPEND && NBUF >= 2 && D <= 128) ? 2 : 1)
   // Lane group c's keys start at block (c >= 2 ? y : x), offset 8*(c&1).
   const int lane_key0 = ((c >= 2) ? kBlock : 0) + 8 * (c & 1);
 
-  // The appended token: this lane's pieces of its K row (the d-slices its
-  // pool K loads cover) and its V values at d = 16*dt + col.
+  // The appended token: in registers, this lane's pieces of its K row (the
+  // d-slices its pool K loads cover) and its V values at d = 16*dt + col.
   const int pos_new = ctx - 1;
   // With two or more pairs in flight the row does not fit in registers next
   // to the ring: each wave keeps it in its own LDS slot instead.
@@ -527,7 +527,6 @@ __global__ __launch_bounds__(NW * 64, (APPEND && NBUF >= 2 && D <= 128) ? 2 : 1)
       }
     }
   }
-
 
   // Per-wave totals: l over the four lane groups of each column.
 #pragma unroll
