@@ -40,6 +40,7 @@
 //
 // Scheduling: workgroup slots with the most keys (last columns of a
 // sequence) are dispatched first.
+#include <atomic>
 #include <type_traits>
 
 #include "pa_device.h"
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ prefix_lens, int num_seqs, int total_q, int max_q_len,
     int num_q_heads, int num_kv_heads, int group, int64_t num_blocks, int max_blocks,
-    int nslots, int slot_shift, float scale_log2) {
+    int nslots, int slot_shift, int fold, float scale_log2) {
   using Cfg = PrefillCfg<D, NT, BK, NW, S>;
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
@@ -145,6 +146,14 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
     // cost at least c" has a closed form.  Lane j handles sequence j
     // (num_seqs <= 64); every wave finds item number bid / Hkv on its own by
     // a binary search over the cost threshold.
+    //
+    // The first `fold` positions are the workgroups that start at once (every
+    // slot of every CU).  Positions p and p + fold/2 land on the same CU, so
+    // that round is folded: position p takes rank p, position p + fold/2
+    // takes rank fold-1-p.  Each CU then holds one long and one short item
+    // instead of two long ones, and the longest items, which bound the
+    // launch when one sequence dominates, get their CU to themselves soon.
+    // Later positions follow the plain longest-first order.
     const int ln = threadIdx.x & 63;
     int ns = 0, pl = 0, la = 0, lb = 0, lp = 0, le0 = -1, le1 = -1;
     // This wave's block of a tile (the same formula as below).
@@ -165,8 +174,11 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
       const int x = (c - 1) * BK - pl;
       return x < 0 ? nsl : (x >= ns ? 0 : nsl - (x >> slot_shift));
     };
-    const int r = bid / num_kv_heads;
-    if (r >= wave_total(nsl)) return;
+    const int items = wave_total(nsl);
+    const int pos = bid / num_kv_heads;
+    if (pos >= items) return;
+    const int nf = min(fold, items), half = nf >> 1;
+    const int r = (pos < half || pos >= nf) ? pos : nf - 1 - (pos - half);
     const int cmax = wave_max_nonneg(nsl > 0 ? (pl + ns + BK - 1) / BK : 0);
     int lo = 1, hi = cmax + 1;  // total(lo) > r >= total(hi)
     while (hi - lo > 1) {
@@ -665,11 +677,28 @@ int launch_cfg(void* out, const void* q, const void* k_cache, const void* v_cach
     slot_shift = 0;
     while ((1 << slot_shift) < Cfg::kCols / group) ++slot_shift;
   }
+  // Workgroups resident at once on this device (CUs x workgroups per CU),
+  // found once per device; in item positions (one position = Hkv workgroups).
+  static std::atomic<int> resident[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -3;
+  int res = resident[dev].load(std::memory_order_relaxed);
+  if (res == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(prefill_kernel<D, NT, BK, NW, S, WPE>), NW * 64,
+            0) != hipSuccess)
+      return -3;
+    res = max(cus * per_cu, 1);
+    resident[dev].store(res, std::memory_order_relaxed);
+  }
+  const int fold = res / num_kv_heads;
   hipLaunchKernelGGL((prefill_kernel<D, NT, BK, NW, S, WPE>), dim3((unsigned)nwg), dim3(NW * 64), 0,
                      stream, (uint16_t*)out, (const uint16_t*)q, (const uint16_t*)k_cache,
                      (const uint16_t*)v_cache, block_tables, cu_seqlens, prefix_lens, num_seqs,
                      total_q, max_q_len, num_q_heads, num_kv_heads, group, num_blocks,
-                     max_blocks_per_seq, (int)nslots, slot_shift, scale * kLog2e);
+                     max_blocks_per_seq, (int)nslots, slot_shift, fold, scale * kLog2e);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
