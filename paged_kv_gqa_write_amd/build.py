@@ -30,6 +30,10 @@ HIPCC_FLAGS = [
     # Packed fp32 instructions stay off: plain fp32 math only.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # The first kernel arguments arrive in SGPRs at wave launch instead of
+    # through a scalar load; the kernels list first what their first memory
+    # loads need.
+    "-mllvm", "-amdgpu-kernarg-preload-count=11",
 ]
 
 

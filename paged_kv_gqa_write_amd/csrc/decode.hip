@@ -293,16 +293,19 @@ __device__ __forceinline__ void store_new_row_lds(uint16_t* k_pool, uint16_t* v_
 // P) live partitions, and its live items come in the order (KV head,
 // partition), as its empty ones do.  When every sequence fills every
 // partition this is the plain order.
+//
+// Parameter order: the first eleven (14 dwords) are preloaded into SGPRs at
+// wave launch; they are what the first loads need (table entries, context
+// length, Q), so those loads do not wait for the kernel-argument fetch.
 template <int D, int NW, int NBUF, int NT, bool APPEND, bool COMPACT>
 __global__ __launch_bounds__(NW * 64, (APPEND && NBUF >= 2 && D <= 128) ? 2 : 1) void decode_kernel(
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
+    const uint16_t* __restrict__ q, int num_partitions, int num_kv_heads, int max_blocks,
+    int blocks_per_part, int num_chunks, int query_len, int group, int num_q_heads,
     uint16_t* __restrict__ out, float* __restrict__ part_out, float* __restrict__ part_lse,
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
-    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
-    const int32_t* __restrict__ context_lens, const uint16_t* __restrict__ k_new,
-    const uint16_t* __restrict__ v_new, uint16_t* k_pool, uint16_t* v_pool, int num_seqs,
-    int query_len, int num_q_heads, int num_kv_heads, int group, int64_t num_blocks,
-    int max_blocks, int blocks_per_part, int num_partitions, int num_chunks,
-    float scale_log2) {
+    const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, uint16_t* k_pool,
+    uint16_t* v_pool, int num_seqs, int64_t num_blocks, float scale_log2) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   int item = blockIdx.x, chunk = 0;
@@ -736,13 +739,12 @@ int launch_decode(void* out, float* part_out, float* part_lse, const void* q,
   // sequence per lane); otherwise the plain order.
   const bool compact = num_partitions > 1 && num_seqs <= 64 && nwg > kComputeUnits;
   auto go = [&](auto kern, int nw) {
-    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(nw * 64), 0, stream, (uint16_t*)out,
-                       part_out, part_lse, (const uint16_t*)q, (const uint16_t*)k_cache,
-                       (const uint16_t*)v_cache, block_tables, context_lens,
-                       (const uint16_t*)k_new, (const uint16_t*)v_new, (uint16_t*)k_cache,
-                       (uint16_t*)v_cache, num_seqs, query_len, num_q_heads, num_kv_heads,
-                       group, num_blocks, max_blocks_per_seq, bpp, num_partitions, chunks,
-                       scale_log2);
+    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(nw * 64), 0, stream, block_tables,
+                       context_lens, (const uint16_t*)q, num_partitions, num_kv_heads,
+                       max_blocks_per_seq, bpp, chunks, query_len, group, num_q_heads,
+                       (uint16_t*)out, part_out, part_lse, (const uint16_t*)k_cache,
+                       (const uint16_t*)v_cache, (const uint16_t*)k_new, (const uint16_t*)v_new,
+                       (uint16_t*)k_cache, (uint16_t*)v_cache, num_seqs, num_blocks, scale_log2);
   };
   // Waves per workgroup (3 or 4) and pairs in flight per wave.  head_dim 128: 3 waves,
   // so that with partitions of 9 pairs (the batch-8 plans) every wave takes

@@ -101,14 +101,17 @@ __device__ __forceinline__ void wait_lds() {
   __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
 
+// The first eleven parameters (14 dwords) are preloaded into SGPRs at wave
+// launch: the work-item search starts from them without waiting for the
+// kernel-argument fetch.
 template <int D, int NT, int BK, int NW, int S, int WPE>
 __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
-    uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
-    const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ prefix_lens, int num_seqs, int total_q, int max_q_len,
-    int num_q_heads, int num_kv_heads, int group, int64_t num_blocks, int max_blocks,
-    int nslots, int slot_shift, int fold, float scale_log2) {
+    int num_kv_heads, int max_blocks, int nslots, int slot_shift, int fold,
+    uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
+    int num_q_heads, int group, int64_t num_blocks, float scale_log2) {
   using Cfg = PrefillCfg<D, NT, BK, NW, S>;
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
@@ -291,11 +294,15 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
   bool bad_entry = false;
   // Table entry of this wave's block in `tile` (block 0 stands in for blocks
   // past the keys needed -- never weighted -- and for bad entries).
+  // Entries are int32: the range check runs in 32 bits on the scalar unit
+  // (a pool of more than 2^31 - 1 blocks holds every non-negative entry).
+  const int nb32 = num_blocks > 0x7FFFFFFF ? 0x7FFFFFFF : (int)num_blocks;
+  const bool huge_pool = num_blocks > 0x7FFFFFFF;
   auto checked_entry = [&](int tile, auto load) __attribute__((always_inline)) -> int64_t {
     const int lb = tile * Cfg::kBlocks + wave_blk;
     if (tile >= ntiles || lb * kBlock >= kend) return 0;
-    const int64_t p = load(lb);
-    if (p < 0 || p >= num_blocks) {
+    const int p = (int)load(lb);
+    if (p < 0 || (!huge_pool && p >= nb32)) {
       bad_entry = true;
       return 0;
     }
@@ -695,10 +702,10 @@ int launch_cfg(void* out, const void* q, const void* k_cache, const void* v_cach
   }
   const int fold = res / num_kv_heads;
   hipLaunchKernelGGL((prefill_kernel<D, NT, BK, NW, S, WPE>), dim3((unsigned)nwg), dim3(NW * 64), 0,
-                     stream, (uint16_t*)out, (const uint16_t*)q, (const uint16_t*)k_cache,
-                     (const uint16_t*)v_cache, block_tables, cu_seqlens, prefix_lens, num_seqs,
-                     total_q, max_q_len, num_q_heads, num_kv_heads, group, num_blocks,
-                     max_blocks_per_seq, (int)nslots, slot_shift, fold, scale * kLog2e);
+                     stream, block_tables, cu_seqlens, prefix_lens, num_seqs, total_q, max_q_len,
+                     num_kv_heads, max_blocks_per_seq, (int)nslots, slot_shift, fold,
+                     (uint16_t*)out, (const uint16_t*)q, (const uint16_t*)k_cache,
+                     (const uint16_t*)v_cache, num_q_heads, group, num_blocks, scale * kLog2e);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
