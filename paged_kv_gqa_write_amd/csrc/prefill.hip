@@ -56,6 +56,9 @@ enum { kFirst = 0, kFixed = 1, kLazy = 2 };
 // Lazy mode: reference-max slack (log2 units) before the accumulators are
 // rescaled.
 constexpr float kRescaleLog2 = 8.f;
+// Columns seeing at least this many keys take plain bf16 weights in the
+// first tile too (see run_pass).
+constexpr int kHiLoMinKeys = 128;
 
 typedef const int32_t __attribute__((address_space(4)))* const_i32_ptr;
 
@@ -605,10 +608,18 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
     // The first tile holds every key of the shortest causal rows, whose
     // outputs are averages of a few values: there P enters the matrix core
     // as a bf16 hi/lo pair so its rounding stays below the output rounding.
-    // It also sets the reference max.  It is peeled off the loop so that the
+    // A wave whose columns all see at least kHiLoMinKeys keys averages the
+    // first tile's rounding like any later tile's and takes the plain form
+    // (each branch passes the one barrier of the tile).  The first tile
+    // also sets the reference max.  It is peeled off the loop so that the
     // loop body carries only the plain forms.
     using no = std::false_type;
-    if (0 < ntiles) step(0, std::integral_constant<int, 0>{}, std::true_type{}, std::true_type{});
+    if (0 < ntiles) {
+      if (wave_min_lim >= kHiLoMinKeys - 1)
+        step(0, std::integral_constant<int, 0>{}, std::true_type{}, no{});
+      else
+        step(0, std::integral_constant<int, 0>{}, std::true_type{}, std::true_type{});
+    }
     for (int t0 = 1; t0 < ntiles; t0 += S) {
       step(t0, std::integral_constant<int, 1 % S>{}, no{}, no{});
       if (t0 + 1 < ntiles) step(t0 + 1, std::integral_constant<int, 2 % S>{}, no{}, no{});
