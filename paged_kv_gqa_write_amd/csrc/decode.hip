@@ -538,12 +538,13 @@ __global__ __launch_bounds__(NW * 64, (APPEND && NBUF >= 2 && D <= 128) ? 2 : 1)
     l_run[nt] = wave_xor_sum(l_run[nt], 32);
   }
 
-  // Merge the NW waves: common max M per column, then waves 1..NW-1 hand
-  // their rescaled accumulators to wave 0 through LDS (fixed order:
-  // deterministic).
+  // Merge the NW waves: common max M per column; every wave hands its
+  // rescaled accumulators to LDS, and wave w then sums and stores the d-tiles
+  // w, w + NW, ... over all waves, adding in wave order from wave 0 (fixed
+  // order: deterministic, and the same sums as one wave adding them all).
   __shared__ float sm_m[NW][NT][16];
   __shared__ float sm_l[NW][NT][16];
-  __shared__ f32x4 sm_o[NW > 1 ? NW - 1 : 1][NT][DT][64];
+  __shared__ f32x4 sm_o[NW > 1 ? NW : 1][NT][DT][64];
   if (lane < 16) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -569,27 +570,25 @@ __global__ __launch_bounds__(NW * 64, (APPEND && NBUF >= 2 && D <= 128) ? 2 : 1)
     for (int dt = 0; dt < DT; ++dt) acc[nt][dt] *= f;
   }
   if (NW > 1) {
-    if (wave > 0) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) sm_o[wave - 1][nt][dt][lane] = acc[nt][dt];
-    }
-    __syncthreads();
-    if (wave > 0) return;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        f32x4 a = acc[nt][dt];
-#pragma unroll
-        for (int w = 0; w < NW - 1; ++w) a += sm_o[w][nt][dt][lane];
-        acc[nt][dt] = a;
-      }
+      for (int dt = 0; dt < DT; ++dt) sm_o[wave][nt][dt][lane] = acc[nt][dt];
+    __syncthreads();
   }
+  // d-tile dt of column tile nt, summed over the waves.
+  auto merged = [&](int nt, int dt) -> f32x4 {
+    if constexpr (NW == 1) {
+      return acc[nt][0 * dt];  // unreachable for NW == 1 (see the loops below)
+    } else {
+      f32x4 a = sm_o[0][nt][dt][lane];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) a += sm_o[w][nt][dt][lane];
+      return a;
+    }
+  };
 
-  // Wave 0 writes: lane (col, c) holds column col of each tile, d = 16*dt +
-  // 4*c + r.
+  // Lane (col, c) holds column col of each tile, d = 16*dt + 4*c + r.
   const float nanv = __builtin_nanf("");
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -598,24 +597,34 @@ __global__ __launch_bounds__(NW * 64, (APPEND && NBUF >= 2 && D <= 128) ? 2 : 1)
     const float inv = L[nt] > 0.f ? 1.f / L[nt] : 0.f;
     if (num_partitions == 1) {
       uint16_t* dst = out + row * D + 4 * c;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        f32x4 o = acc[nt][dt] * inv;
+      auto put = [&](int dt, f32x4 a) {
+        f32x4 o = a * inv;
         if (any_bad) o = f32x4{nanv, nanv, nanv, nanv};
         u32x2 w;
         w[0] = pack_bf16x2(o[0], o[1]);
         w[1] = pack_bf16x2(o[2], o[3]);
         *reinterpret_cast<u32x2*>(dst + 16 * dt) = w;
+      };
+      if constexpr (NW == 1) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) put(dt, acc[nt][dt]);
+      } else {
+        for (int dt = wave; dt < DT; dt += NW) put(dt, merged(nt, dt));
       }
     } else {
       float* dst = part_out + (row * num_partitions + p) * D + 4 * c;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        f32x4 o = acc[nt][dt] * inv;
+      auto put = [&](int dt, f32x4 a) {
+        f32x4 o = a * inv;
         if (any_bad) o = f32x4{nanv, nanv, nanv, nanv};
         *reinterpret_cast<f32x4*>(dst + 16 * dt) = o;
+      };
+      if constexpr (NW == 1) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) put(dt, acc[nt][dt]);
+      } else {
+        for (int dt = wave; dt < DT; dt += NW) put(dt, merged(nt, dt));
       }
-      if (c == 0) {
+      if (wave == 0 && c == 0) {
         float lse = L[nt] > 0.f ? (M[nt] + fast_log2(L[nt])) * kLn2 : -INFINITY;
         if (any_bad) lse = nanv;
         part_lse[row * num_partitions + p] = lse;
