@@ -632,7 +632,6 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
 
   run_pass(std::integral_constant<int, kFixed>{}, true);
 
-  const bool any_bad = __syncthreads_or(bad || bad_entry);
   // The fixed-reference pass is exact unless a score rose more than 2^64
   // above its column's first-tile max (or something overflowed): then the
   // workgroup runs again with the lazily rescaled reference.
@@ -646,7 +645,20 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) redo |= !(fabsf(acc[nt][dt][e]) < INFINITY);
   }
-  if (__syncthreads_or(redo && !any_bad)) {
+  // Both flags over the workgroup in one exchange: a ballot per wave, one LDS
+  // word per wave, one barrier (which also ends every wave's reads of the
+  // stage buffers before a re-run copies into them).
+  __shared__ int sm_flags[NW];
+  {
+    const int f = (__ballot(bad || bad_entry) != 0 ? 1 : 0) | (__ballot(redo) != 0 ? 2 : 0);
+    if (lane == 0) sm_flags[wave] = f;
+  }
+  __syncthreads();
+  int flags = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) flags |= sm_flags[w];
+  const bool any_bad = (flags & 1) != 0;
+  if ((flags & 2) != 0 && !any_bad) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       l_acc[nt] = f32x4{0, 0, 0, 0};
