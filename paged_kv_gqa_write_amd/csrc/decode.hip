@@ -542,8 +542,10 @@ __global__ __launch_bounds__(NW * 64, (APPEND && NBUF >= 2 && D <= 128) ? 2 : 1)
   // rescaled accumulators to LDS, and wave w then sums and stores the d-tiles
   // w, w + NW, ... over all waves, adding in wave order from wave 0 (fixed
   // order: deterministic, and the same sums as one wave adding them all).
+  // The bad flag travels with each wave's (m, l): one barrier for both.
   __shared__ float sm_m[NW][NT][16];
   __shared__ float sm_l[NW][NT][16];
+  __shared__ int sm_bad[NW];
   __shared__ f32x4 sm_o[NW > 1 ? NW : 1][NT][DT][64];
   if (lane < 16) {
 #pragma unroll
@@ -552,7 +554,14 @@ __global__ __launch_bounds__(NW * 64, (APPEND && NBUF >= 2 && D <= 128) ? 2 : 1)
       sm_l[wave][nt][col] = l_run[nt];
     }
   }
-  const bool any_bad = __syncthreads_or(bad);
+  {
+    const int wb = __ballot(bad) != 0 ? 1 : 0;
+    if (lane == 0) sm_bad[wave] = wb;
+  }
+  __syncthreads();
+  bool any_bad = false;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) any_bad |= sm_bad[w] != 0;
   float M[NT], L[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
