@@ -119,8 +119,13 @@ __device__ __forceinline__ void compute_pair(PairRegs<D>& r, const u32x4 (&qf)[N
     float mx = sc[0];
 #pragma unroll
     for (int t = 1; t < 8; ++t) mx = fmaxf(mx, sc[t]);
-    mx = wave_xor_max(mx, 16);
-    mx = wave_xor_max(mx, 32);
+    if constexpr (D <= 128) {  // head_dim 256: the shuffle form measured faster
+      mx = xor16_max(mx);
+      mx = xor32_max(mx);
+    } else {
+      mx = wave_xor_max(mx, 16);
+      mx = wave_xor_max(mx, 32);
+    }
     const float m_new = fmaxf(m_run[nt], mx);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     alpha[nt] = fast_exp2(m_run[nt] - m_use);
@@ -534,8 +539,13 @@ __global__ __launch_bounds__(NW * 64, (APPEND && NBUF >= 2 && D <= 128) ? 2 : 1)
   // Per-wave totals: l over the four lane groups of each column.
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    l_run[nt] = wave_xor_sum(l_run[nt], 16);
-    l_run[nt] = wave_xor_sum(l_run[nt], 32);
+    if constexpr (D <= 128) {
+      l_run[nt] = xor16_sum(l_run[nt]);
+      l_run[nt] = xor32_sum(l_run[nt]);
+    } else {
+      l_run[nt] = wave_xor_sum(l_run[nt], 16);
+      l_run[nt] = wave_xor_sum(l_run[nt], 32);
+    }
   }
 
   // Merge the NW waves: common max M per column; every wave hands its

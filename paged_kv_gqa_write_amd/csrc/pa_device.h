@@ -61,6 +61,28 @@ __device__ __forceinline__ float wave_xor_sum(float v, int mask) {
   return v + __shfl_xor(v, mask, kWave);
 }
 
+// v combined with lane l ^ 16 (rows of 16 lanes) or l ^ 32 (halves of the
+// wave) on the vector ALU.  Swapping a register's rows (halves) with a copy of
+// itself leaves each lane its own value and its partner's, in one order or the
+// other; max and + are commutative, so the results equal the shuffle forms
+// above, bit for bit, without a trip through the LDS crossbar.
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Uniform (scalar) copy of a wave-uniform value.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

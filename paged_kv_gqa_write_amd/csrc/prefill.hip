@@ -418,16 +418,16 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
         if constexpr (MODE == kFirst) {
           // Max over the column's four lane groups; a column that sees no key
           // (past the sequence, never written) takes 0.
-          float mall = wave_xor_max(mx, 16);
-          mall = wave_xor_max(mall, 32);
+          float mall = xor16_max(mx);
+          mall = xor32_max(mall);
           m_run[nt] = (mall == -INFINITY) ? 0.f : mall;
         } else {
           // The test is per lane but the update is wave-uniform; the new max
           // is reduced over the column's four lane groups, so m_run stays
           // equal across them.
           if (__any(mx > m_run[nt] + kRescaleLog2)) {
-            float mall = wave_xor_max(mx, 16);
-            mall = wave_xor_max(mall, 32);
+            float mall = xor16_max(mx);
+            mall = xor32_max(mall);
             const float m_new = fmaxf(m_run[nt], mall);
             const float alpha = fast_exp2(m_run[nt] - m_new);
             l_acc[nt] *= alpha;
