@@ -788,7 +788,13 @@ int launch_decode(void* out, float* part_out, float* part_lse, const void* q,
   // batch 64 at 36 pairs: 52.0 -> 51.2 us, batch 4 x 8192 at 32: 25.5 ->
   // 25.1; plain, batch 64: 49.8 -> 49.1, 16 x 8192 in 2 x 4096: 87.3 ->
   // 85.5).  The two forms split partitions alike, so they give bit-identical
-  // results.
+  // results.  head_dim 256: 4 waves; the plain form keeps 2 pairs in flight,
+  // the appending form 1 with its row in registers.  With 2, the appending
+  // wave must wait for both pairs before it can copy its row into LDS, and
+  // every wave of the launch then waits for the whole first burst (hybrid
+  // batch 25.27 -> 24.93 us, 32 x 1024 18.07 -> 16.79, 64 x 512 29.56 ->
+  // 28.57, 4 x 16384 27.14 -> 26.70; the plain form loses with 1: 24.71 ->
+  // 26.25 on the hybrid batch).
   auto pick = [&](auto compact_tag) {
     constexpr bool C = decltype(compact_tag)::value;
     switch (head_dim * 8 + nt * 2 + (append ? 1 : 0)) {
@@ -806,7 +812,7 @@ int launch_decode(void* out, float* part_out, float* part_lse, const void* q,
         return 0;
       case 256 * 8 + 2: go(decode_kernel<256, 4, 2, 1, false, C>, 4); return 0;
       case 256 * 8 + 4: go(decode_kernel<256, 4, 1, 2, false, C>, 4); return 0;
-      case 256 * 8 + 3: go(decode_kernel<256, 4, 2, 1, true, C>, 4); return 0;
+      case 256 * 8 + 3: go(decode_kernel<256, 4, 1, 1, true, C>, 4); return 0;
       default: return -2;
     }
   };
