@@ -513,11 +513,16 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
         ka[i] = *reinterpret_cast<const u32x4*>(kr);
         kb[i] = *reinterpret_cast<const u32x4*>(kr + 4 * (2 * D));
       };
-      kread(0);
+      // K reads in flight ahead of the products: two steps at head_dim 256
+      // (two waves per SIMD leave registers for it and little else to hide the
+      // LDS latency), one at head_dim 64/128 (the 128-register cap).
+      constexpr int KA = D >= 256 ? 2 : 1;
+#pragma unroll
+      for (int i = 0; i < KA; ++i) kread(i);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < KS; ++i) {
-        if (i + 1 < KS) kread(i + 1);
+        if (i + KA < KS) kread(i + KA);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
