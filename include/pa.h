@@ -57,7 +57,9 @@
  *     included).  The product num_partitions*partition_size must stay below
  *     2^31 - 64 (PA_ERR_UNSUPPORTED otherwise).
  *   Supported shapes: head_dim in {64, 128, 256}; num_q_heads a multiple of
- *     num_kv_heads with a group Hq/Hkv of at most 16; block_size == 16.
+ *     num_kv_heads with a group Hq/Hkv of at most 16; block_size == 16;
+ *     num_kv_heads at most 65535 for pa_write_kv, pa_copy_blocks and
+ *     pa_prefill (PA_ERR_UNSUPPORTED otherwise).
  *   Sizes of 0 (no tokens, no sequences) are valid no-ops.
  */
 #ifndef PAGED_KV_GQA_PA_H

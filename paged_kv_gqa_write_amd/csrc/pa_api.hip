@@ -209,6 +209,8 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
   if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || num_blocks < 0) return PA_ERR_INVALID_ARG;
   int st = check_heads(num_q_heads, num_kv_heads, head_dim, block_size);
   if (st != PA_OK) return st;
+  // The kernel forms a block's element offset as a 32-bit product.
+  if (num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
   if (max_blocks_per_seq <= 0) return PA_ERR_INVALID_ARG;
   if (!isfinite(scale) || scale < 0.f) return PA_ERR_INVALID_ARG;
   if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PA_OK;

@@ -140,7 +140,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
   int slot, s, q0, q1, P;
   // Table entries of this wave's block in tiles 0 and 1, fetched with the
   // sequence lengths when the longest-first order is computed (-1: none).
-  int64_t pre0 = -1, pre1 = -1;
+  int pre0 = -1, pre1 = -1;
   bool have_pre = false;
   if (slot_shift >= 0) {
     // Longest-first order of the (sequence, slot) work items.  The hardware
@@ -265,6 +265,12 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) wave_min_lim = min(wave_min_lim, __shfl_xor(wave_min_lim, m, 64));
   wave_min_lim = __builtin_amdgcn_readfirstlane(wave_min_lim);
+  // A pair takes the masked form when it crosses a causal limit of one of this
+  // wave's columns or reaches past kend (pair0 + 31 > wave_min_lim or
+  // pair0 + 32 > kend), i.e. from pair0 = pmask on.
+  const int pmask = min(wave_min_lim - 31, kend - 32) + 1;
+  // The last tile when it reaches past kend (its V^T tail is zeroed), else -1.
+  const int tail_tile = ntiles * BK > kend ? ntiles - 1 : -1;
 
   f32x4 acc[NT][DT];
 #pragma unroll
@@ -299,28 +305,35 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
   // past the keys needed -- never weighted -- and for bad entries).
   // Entries are int32: the range check runs in 32 bits on the scalar unit
   // (a pool of more than 2^31 - 1 blocks holds every non-negative entry).
-  const int nb32 = num_blocks > 0x7FFFFFFF ? 0x7FFFFFFF : (int)num_blocks;
-  const bool huge_pool = num_blocks > 0x7FFFFFFF;
-  auto checked_entry = [&](int tile, auto load) __attribute__((always_inline)) -> int64_t {
-    const int lb = tile * Cfg::kBlocks + wave_blk;
-    if (tile >= ntiles || lb * kBlock >= kend) return 0;
-    const int p = (int)load(lb);
-    if (p < 0 || (!huge_pool && p >= nb32)) {
+  // One unsigned compare: a negative entry reads as 2^31 or more.
+  const uint32_t nb_lim = num_blocks > 0x7FFFFFFF ? 0x80000000u : (uint32_t)num_blocks;
+  // The wave's block of a tile holds needed keys for tiles below tlim_w:
+  // block tile*kBlocks + wave_blk starts below kend.
+  const int nblk_need = (kend + kBlock - 1) / kBlock;
+  const int tlim_w = nblk_need > wave_blk ? (nblk_need - wave_blk + Cfg::kBlocks - 1) / Cfg::kBlocks : 0;
+  auto checked_entry = [&](int tile, auto load) __attribute__((always_inline)) -> int {
+    if (tile >= tlim_w) return 0;
+    const int p = (int)load(tile * Cfg::kBlocks + wave_blk);
+    if ((uint32_t)p >= nb_lim) {
       bad_entry = true;
       return 0;
     }
     return p;
   };
-  auto entry_of = [&](int tile) __attribute__((always_inline)) -> int64_t {
-    return checked_entry(tile, [&](int lb) -> int64_t { return btc[lb]; });
+  auto entry_of = [&](int tile) __attribute__((always_inline)) -> int {
+    return checked_entry(tile, [&](int lb) -> int { return btc[lb]; });
   };
   // Tiles 0 and 1 from the prefetched entries where there are some.
-  auto first_entry = [&](int tile) __attribute__((always_inline)) -> int64_t {
+  auto first_entry = [&](int tile) __attribute__((always_inline)) -> int {
     if (!have_pre) return entry_of(tile);
-    return checked_entry(tile, [&](int) -> int64_t { return tile == 0 ? pre0 : pre1; });
+    return checked_entry(tile, [&](int) -> int { return tile == 0 ? pre0 : pre1; });
   };
-  auto issue = [&](int64_t phys, uint8_t* sb) __attribute__((always_inline)) {
-    const int64_t tile_base = (phys * num_kv_heads + g) * (int64_t)(kBlock * D);
+  // Element offset of (block, KV head g): a 32 x 32 -> 64-bit product (the
+  // launcher checks that a block of all KV heads spans fewer than 2^31 elements).
+  const uint32_t blk_elems = (uint32_t)num_kv_heads * (uint32_t)(kBlock * D);
+  const uint32_t g_elems = (uint32_t)g * (uint32_t)(kBlock * D);
+  auto issue = [&](int phys, uint8_t* sb) __attribute__((always_inline)) {
+    const uint64_t tile_base = (uint64_t)(uint32_t)phys * blk_elems + g_elems;
     const uint16_t* kt = uniform_ptr(k_cache + tile_base);
     const uint16_t* vt = uniform_ptr(v_cache + tile_base);
 #pragma unroll
@@ -542,7 +555,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
       if (FIRST && kp == 0) {
         softmax_pair(key0, s0, s1, pb, pl, std::integral_constant<int, kFirst>{}, std::true_type{},
                      hilo_tag);
-      } else if (pair0 + 31 > wave_min_lim || pair0 + 32 > kend) {
+      } else if (pair0 >= pmask) {
         softmax_pair(key0, s0, s1, pb, pl, mode_tag, std::true_type{}, hilo_tag);
       } else {
         softmax_pair(key0, s0, s1, pb, pl, mode_tag, std::false_type{}, hilo_tag);
@@ -574,7 +587,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
       if (1 < ntiles) issue(entry_of(1), stage(std::integral_constant<int, 1>{}));
     if constexpr (S >= 4)
       if (2 < ntiles) issue(entry_of(2), stage(std::integral_constant<int, 2>{}));
-    int64_t next_phys = entry_of(S == 2 ? 2 : S - 1);
+    int next_phys = entry_of(S == 2 ? 2 : S - 1);
     auto step = [&](int t, auto stage_tag, auto first_tag, auto hilo_tag)
         __attribute__((always_inline)) {
       constexpr int ST = decltype(stage_tag)::value;
@@ -587,12 +600,12 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
         if (ahead >= 1) wait_vm<KPW + VPW>();
         else wait_vm<0>();
       } else {
-        if (t == 0 && 1 < ntiles) wait_vm<KPW + VPW>();  // tile 1 may stay in flight
+        if (decltype(first_tag)::value && 1 < ntiles) wait_vm<KPW + VPW>();  // tile 1 may stay in flight
         else wait_vm<0>();
       }
       // Last tile: zero the V^T values of keys at or past kend in this wave's
       // own copies (complete after the wait above) before publishing them.
-      if (t == ntiles - 1 && t * BK + BK > kend) {
+      if (t == tail_tile) {
         zero_v_tail(t, stage(std::integral_constant<int, ST>{}));
         wait_lds();
       }
@@ -600,7 +613,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
       run_tile(t, stage(std::integral_constant<int, ST>{}), first_tag, mode_tag, hilo_tag,
                [&]() __attribute__((always_inline)) {
                  if constexpr (S == 2) {
-                   if (t >= 1 && t + 1 < ntiles) {
+                   if (!decltype(first_tag)::value && t + 1 < ntiles) {
                      issue(next_phys, stage(std::integral_constant<int, (ST + 1) % 2>{}));
                      next_phys = entry_of(t + 2);
                    }

@@ -84,6 +84,7 @@ def test_write_kv_validation(lib):
     assert _write(lib, nb=-5) == INVALID
     assert _write(lib, d=96) == UNSUPPORTED
     assert _write(lib, bs=32) == UNSUPPORTED
+    assert _write(lib, hkv=65536) == UNSUPPORTED
     assert _write(lib, k_new=None) == INVALID
     assert _write(lib, slots=None) == INVALID
     assert _write(lib, vc=None) == INVALID
@@ -237,6 +238,7 @@ def _copy(lib, **kw):
 def test_copy_blocks_validation(lib):
     assert _copy(lib, n=-1) == INVALID
     assert _copy(lib, hkv=0) == INVALID
+    assert _copy(lib, hkv=65536) == UNSUPPORTED
     assert _copy(lib, dnb=-1) == INVALID
     assert _copy(lib, snb=-2) == INVALID
     assert _copy(lib, d=100) == UNSUPPORTED
@@ -267,6 +269,7 @@ def test_prefill_validation(lib):
     assert _prefill(lib, hq=33) == INVALID
     assert _prefill(lib, d=512) == UNSUPPORTED
     assert _prefill(lib, bs=64) == UNSUPPORTED
+    assert _prefill(lib, hq=65536, hkv=65536) == UNSUPPORTED  # 32-bit block offsets
     assert _prefill(lib, mb=0) == INVALID
     assert _prefill(lib, scale=float("nan")) == INVALID
     assert _prefill(lib, scale=-1.0) == INVALID
