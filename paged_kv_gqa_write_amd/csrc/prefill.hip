@@ -488,12 +488,19 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
     auto vread = [&](int dt) __attribute__((always_inline)) {
       a[dt] = *reinterpret_cast<const u32x4*>(vr + dt * (16 * 32));
     };
-    vread(0);
-    if (DT > 1) vread(1);
+    // V^T reads in flight ahead of the products.  While a tile copy into LDS
+    // is in flight (from the first pair's score products to the next tile),
+    // the compiler waits for all outstanding LDS reads at each use of a read
+    // result, so a deeper read-ahead makes those full waits rarer: ten ahead
+    // at head_dim 256 (register room at two waves per SIMD), two elsewhere.
+    constexpr int VA = D >= 256 ? 10 : 2;
+#pragma unroll
+    for (int i = 0; i < VA; ++i)
+      if (i < DT) vread(i);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      if (dt + 2 < DT) vread(dt + 2);
+      if (dt + VA < DT) vread(dt + VA);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
