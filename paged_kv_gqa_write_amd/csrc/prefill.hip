@@ -513,9 +513,11 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
 
   // FIRST: this is tile 0, whose first pair sets the reference max; the
   // tile's other pairs and all later tiles run in the pass's mode.
-  // after_qk runs once per tile, right after the first pair's score products
-  // are issued (the next tile's copies start there, off the path from the
-  // barrier to the first LDS reads).
+  // after_qk runs once per tile, right after the last pair's score products
+  // are issued: the next tile's copies start there, off the path from the
+  // barrier to the first LDS reads, and late enough that the earlier pairs'
+  // LDS reads keep counted waits (with a copy into LDS in flight the compiler
+  // waits for every outstanding LDS read).
   auto run_tile = [&](int tile, const uint8_t* sb, auto first_tag, auto mode_tag, auto hilo_tag,
                       auto&& after_qk) __attribute__((always_inline)) {
     constexpr bool FIRST = decltype(first_tag)::value;
@@ -551,7 +553,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (kp == 0) after_qk();
+      if (kp == BK / 32 - 1) after_qk();
       // Lane group c holds keys key0 + 0..7 (0..3 from s0, 4..7 from s1).
       const int pair0 = tile * BK + 32 * kp;
       const int key0 = pair0 + 8 * c;
