@@ -519,8 +519,9 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
   // LDS reads keep counted waits (with a copy into LDS in flight the compiler
   // waits for every outstanding LDS read).
   auto run_tile = [&](int tile, const uint8_t* sb, auto first_tag, auto mode_tag, auto hilo_tag,
-                      auto&& after_qk) __attribute__((always_inline)) {
+                      auto plain_tag, auto&& after_qk) __attribute__((always_inline)) {
     constexpr bool FIRST = decltype(first_tag)::value;
+    constexpr bool PLAIN = decltype(plain_tag)::value;  // every pair of the tile is plain
 #pragma unroll
     for (int kp = 0; kp < BK / 32; ++kp) {
       f32x4 s0[NT], s1[NT];
@@ -561,7 +562,9 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
       // wave's columns, or reach past the keys this workgroup needs?
       u32x4 pb[NT], pl[NT];
       __builtin_amdgcn_sched_barrier(0);
-      if (FIRST && kp == 0) {
+      if constexpr (PLAIN) {
+        softmax_pair(key0, s0, s1, pb, pl, mode_tag, std::false_type{}, hilo_tag);
+      } else if (FIRST && kp == 0) {
         softmax_pair(key0, s0, s1, pb, pl, std::integral_constant<int, kFirst>{}, std::true_type{},
                      hilo_tag);
       } else if (pair0 >= pmask) {
@@ -597,7 +600,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
     if constexpr (S >= 4)
       if (2 < ntiles) issue(entry_of(2), stage(std::integral_constant<int, 2>{}));
     int next_phys = entry_of(S == 2 ? 2 : S - 1);
-    auto step = [&](int t, auto stage_tag, auto first_tag, auto hilo_tag)
+    auto step = [&](int t, auto stage_tag, auto first_tag, auto hilo_tag, auto plain_tag)
         __attribute__((always_inline)) {
       constexpr int ST = decltype(stage_tag)::value;
       const int ahead = min(S - 2, ntiles - 1 - t);  // tiles issued after t
@@ -614,12 +617,12 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
       }
       // Last tile: zero the V^T values of keys at or past kend in this wave's
       // own copies (complete after the wait above) before publishing them.
-      if (t == tail_tile) {
+      if (!decltype(plain_tag)::value && t == tail_tile) {
         zero_v_tail(t, stage(std::integral_constant<int, ST>{}));
         wait_lds();
       }
       __builtin_amdgcn_s_barrier();
-      run_tile(t, stage(std::integral_constant<int, ST>{}), first_tag, mode_tag, hilo_tag,
+      run_tile(t, stage(std::integral_constant<int, ST>{}), first_tag, mode_tag, hilo_tag, plain_tag,
                [&]() __attribute__((always_inline)) {
                  if constexpr (S == 2) {
                    if (!decltype(first_tag)::value && t + 1 < ntiles) {
@@ -643,17 +646,31 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
     using no = std::false_type;
     if (0 < ntiles) {
       if (wave_min_lim >= kHiLoMinKeys - 1)
-        step(0, std::integral_constant<int, 0>{}, std::true_type{}, no{});
+        step(0, std::integral_constant<int, 0>{}, std::true_type{}, no{}, no{});
       else
-        step(0, std::integral_constant<int, 0>{}, std::true_type{}, std::true_type{});
+        step(0, std::integral_constant<int, 0>{}, std::true_type{}, std::true_type{}, no{});
     }
-    for (int t0 = 1; t0 < ntiles; t0 += S) {
-      step(t0, std::integral_constant<int, 1 % S>{}, no{}, no{});
-      if (t0 + 1 < ntiles) step(t0 + 1, std::integral_constant<int, 2 % S>{}, no{}, no{});
+    int t0 = 1;
+    if constexpr (S == 2) {
+      // Tiles below tplain hold only plain pairs for this wave (the last
+      // pair of tile t starts at t*BK + BK - 32 < pmask): a loop without
+      // the masked forms or the tail test.  Waves may leave it at different
+      // tiles; every wave still passes one barrier per tile.
+      const int xp = pmask - BK + 32;
+      const int tplain = min(ntiles, xp > 0 ? (xp + BK - 1) / BK : 0);
+      using yes = std::true_type;
+      for (; t0 + 1 < tplain; t0 += 2) {
+        step(t0, std::integral_constant<int, 1>{}, no{}, no{}, yes{});
+        step(t0 + 1, std::integral_constant<int, 0>{}, no{}, no{}, yes{});
+      }
+    }
+    for (; t0 < ntiles; t0 += S) {
+      step(t0, std::integral_constant<int, 1 % S>{}, no{}, no{}, no{});
+      if (t0 + 1 < ntiles) step(t0 + 1, std::integral_constant<int, 2 % S>{}, no{}, no{}, no{});
       if constexpr (S >= 3)
-        if (t0 + 2 < ntiles) step(t0 + 2, std::integral_constant<int, 3 % S>{}, no{}, no{});
+        if (t0 + 2 < ntiles) step(t0 + 2, std::integral_constant<int, 3 % S>{}, no{}, no{}, no{});
       if constexpr (S >= 4)
-        if (t0 + 3 < ntiles) step(t0 + 3, std::integral_constant<int, 4 % S>{}, no{}, no{});
+        if (t0 + 3 < ntiles) step(t0 + 3, std::integral_constant<int, 4 % S>{}, no{}, no{}, no{});
     }
   };
 
