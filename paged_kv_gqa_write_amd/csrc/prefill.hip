@@ -659,11 +659,13 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
       const int xp = pmask - BK + 32;
       const int tplain = min(ntiles, xp > 0 ? (xp + BK - 1) / BK : 0);
       using yes = std::true_type;
+      wait_lds();  // no scalar load left pending into the loop
       for (; t0 + 1 < tplain; t0 += 2) {
         step(t0, std::integral_constant<int, 1>{}, no{}, no{}, yes{});
         step(t0 + 1, std::integral_constant<int, 0>{}, no{}, no{}, yes{});
       }
     }
+    wait_lds();
     for (; t0 < ntiles; t0 += S) {
       step(t0, std::integral_constant<int, 1 % S>{}, no{}, no{}, no{});
       if (t0 + 1 < ntiles) step(t0 + 1, std::integral_constant<int, 2 % S>{}, no{}, no{}, no{});
