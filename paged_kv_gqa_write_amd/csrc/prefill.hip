@@ -259,12 +259,11 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
 
   // Smallest causal limit over the wave's columns that are written (columns
   // past the sequence take whatever the plain form gives; never stored).
-  int wave_min_lim = 0x7FFFFFFF;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) wave_min_lim = min(wave_min_lim, lim[nt] < 0 ? 0x7FFFFFFF : lim[nt]);
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) wave_min_lim = min(wave_min_lim, __shfl_xor(wave_min_lim, m, 64));
-  wave_min_lim = __builtin_amdgcn_readfirstlane(wave_min_lim);
+  // Columns grow with the lane and the tile, and so do their limits: lane 0's
+  // first column has the smallest, and it is written whenever any column of
+  // the wave is.
+  const int lim0 = __builtin_amdgcn_readfirstlane(lim[0]);
+  const int wave_min_lim = lim0 < 0 ? 0x7FFFFFFF : lim0;
   // A pair takes the masked form when it crosses a causal limit of one of this
   // wave's columns or reaches past kend (pair0 + 31 > wave_min_lim or
   // pair0 + 32 > kend), i.e. from pair0 = pmask on.
