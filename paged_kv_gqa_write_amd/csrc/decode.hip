@@ -802,7 +802,11 @@ int launch_decode(void* out, float* part_out, float* part_lse, const void* q,
       case 64 * 8 + 4: go(decode_kernel<64, 4, 4, 2, false, C>, 4); return 0;
       case 64 * 8 + 3: go(decode_kernel<64, 4, 4, 1, true, C>, 4); return 0;
       case 128 * 8 + 2:
-        if (bpp >= 64) go(decode_kernel<128, 4, 2, 1, false, C>, 4);
+        // Partitions of 32+ pairs: a second pair in flight pays only when two
+        // workgroups share a CU (batch 64: 49.31 -> 48.50 us); with one
+        // workgroup per CU one pair is faster (4 x 8192: 25.04 -> 24.44 us).
+        if (bpp >= 64 && nwg <= kComputeUnits) go(decode_kernel<128, 4, 1, 1, false, C>, 4);
+        else if (bpp >= 64) go(decode_kernel<128, 4, 2, 1, false, C>, 4);
         else go(decode_kernel<128, 3, 2, 1, false, C>, 3);
         return 0;
       case 128 * 8 + 4: go(decode_kernel<128, 3, 2, 2, false, C>, 3); return 0;
