@@ -640,8 +640,8 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
     // A wave whose columns all see at least kHiLoMinKeys keys averages the
     // first tile's rounding like any later tile's and takes the plain form
     // (each branch passes the one barrier of the tile).  The first tile
-    // also sets the reference max.  It is peeled off the loop so that the
-    // loop body carries only the plain forms.
+    // also sets the reference max.  It is peeled off so that the loops below
+    // carry neither the first-tile softmax nor the hi/lo products.
     using no = std::false_type;
     if (0 < ntiles) {
       if (wave_min_lim >= kHiLoMinKeys - 1)
