@@ -409,9 +409,10 @@ def restore_leg(c):
     torch, lib, dev, sptr, args = c.torch, c.lib, c.dev, c.sptr, c.args
     hkv, d, n, nb, nh = 8, 128, 1024, 4096, 8
     blk = hkv * 16 * d * 2
-    kc = torch.empty((nb, hkv, 16, d), dtype=torch.bfloat16, device=dev)
+    kc = torch.empty((nb, hkv, d // 32, 16, 32), dtype=torch.bfloat16, device=dev)
     vc = torch.empty((nb, hkv, d, 16), dtype=torch.bfloat16, device=dev)
-    hk = [torch.zeros((n, hkv, 16, d), dtype=torch.bfloat16, pin_memory=True) for _ in range(nh)]
+    hk = [torch.zeros((n, hkv, d // 32, 16, 32), dtype=torch.bfloat16, pin_memory=True)
+          for _ in range(nh)]
     hv = [torch.zeros((n, hkv, d, 16), dtype=torch.bfloat16, pin_memory=True) for _ in range(nh)]
     g = torch.Generator(device=dev)
     g.manual_seed(7)

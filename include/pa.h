@@ -24,8 +24,11 @@
  * Memory layout (all tensors row-major and contiguous; bf16 = 16-bit storage)
  * ---------------------------------------------------------------------------
  *   block_size (BS) is 16 tokens.
- *   K pool   [num_blocks, Hkv, 16, D]  bf16: K row of the token at in-block
- *            offset o of block b for KV head g starts at ((b*Hkv+g)*16+o)*D.
+ *   K pool   [num_blocks, Hkv, D/32, 16, 32]  bf16: the head dimension is
+ *            cut into 32-wide slices and each slice holds the block's 16
+ *            keys as 64-byte rows -- element d of the K row of the token at
+ *            in-block offset o of block b for KV head g is at
+ *            (((b*Hkv+g)*(D/32) + d/32)*16 + o)*32 + d%32.
  *   V pool   [num_blocks, Hkv, D, 16]  bf16: "transposed" -- element d of
  *            that token's V row is at ((b*Hkv+g)*D+d)*16+o.  Each (block,
  *            head) of either pool is one contiguous 16*D*2-byte tile.
@@ -299,7 +302,7 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
  *
  * For every i in [0, num_copies):
  *   destination block dst_block_ids[i] := source block src_block_ids[i]
- * for both pools (the whole [Hkv, 16, D] K tile and [Hkv, D, 16] V tile,
+ * for both pools (the whole [Hkv, D/32, 16, 32] K tile and [Hkv, D, 16] V tile,
  * bit for bit).  A NULL id array means "block i" for copy i, i.e. a packed
  * run of num_copies blocks in the pool layout.  A copy whose source id is
  * outside [0, src_num_blocks) or whose destination id is outside

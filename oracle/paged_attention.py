@@ -37,8 +37,11 @@ What is computed (the pages print no formula; this is the plainest reading):
     changes nothing mathematically).
 
 Layout contract (also defined by the library header):
-  K pool [NB, Hkv, 16, D]: K of the token in (block b, offset o) for KV head g
-      is k_cache[b, g, o, :].
+  K pool [NB, Hkv, D/W, 16, W] with slice width W = 32 in the library: K of
+      the token in (block b, offset o) for KV head g is k_cache[b, g, :, o, :]
+      read slice by slice, element d at k_cache[b, g, d // W, o, d % W].  W
+      is taken from the pool's last axis, so tiny cases whose D is not a
+      multiple of 32 use a single slice of width D.
   V pool [NB, Hkv, D, 16]: V of that token is v_cache[b, g, :, o].
   slot id = b * 16 + o; a negative slot means "do not write".
 
@@ -102,8 +105,10 @@ def token_location(block_table_row, pos: int):
 
 
 def read_k(k_cache, block: int, off: int):
-    """K rows of all KV heads of one token: [Hkv, D]."""
-    return k_cache[block, :, off, :]
+    """K rows of all KV heads of one token: [Hkv, D] (the D/W slices in
+    order)."""
+    hkv = k_cache.shape[1]
+    return k_cache[block, :, :, off, :].reshape(hkv, -1)
 
 
 def read_v(v_cache, block: int, off: int):
@@ -133,7 +138,7 @@ def gather_sequence(k_cache, v_cache, block_table_row, n: int):
     Only the n live positions are touched; nothing else in the pool (unused
     blocks, tails, table padding) is read.
     """
-    hkv, d = k_cache.shape[1], k_cache.shape[3]
+    hkv, d = k_cache.shape[1], k_cache.shape[2] * k_cache.shape[4]
     K = np.empty((n, hkv, d), dtype=np.float64)
     V = np.empty((n, hkv, d), dtype=np.float64)
     for p in range(n):
@@ -191,7 +196,7 @@ def write_kv(k_cache, v_cache, k_new, v_new, slot_mapping):
         if slot < 0:
             continue
         b, o = slot_location(slot)
-        kc[b, :, o, :] = k_new[t]
+        kc[b, :, :, o, :] = np.asarray(k_new[t]).reshape(kc.shape[1], kc.shape[2], kc.shape[4])
         vc[b, :, :, o] = v_new[t]
     return kc, vc
 
@@ -347,8 +352,8 @@ def decode_multi_partials(q, k_cache, v_cache, block_tables, context_lens, scale
 def copy_blocks(dst_k, dst_v, dst_ids, src_k, src_v, src_ids, num_copies):
     """Block-granular KV copy.  For i in [0, num_copies): destination block
     dst_ids[i] (block i when dst_ids is None) receives source block
-    src_ids[i] (block i when src_ids is None) -- the whole [Hkv, 16, D] K
-    tile and [Hkv, D, 16] V tile, bit for bit.  A copy whose source or
+    src_ids[i] (block i when src_ids is None) -- the whole [Hkv, D/W, 16, W]
+    K tile and [Hkv, D, 16] V tile, bit for bit.  A copy whose source or
     destination id lies outside its pool is skipped.  Returns new destination
     pools (uint16 bit patterns)."""
     dk = np.array(dst_k, copy=True)

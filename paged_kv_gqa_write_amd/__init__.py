@@ -7,7 +7,9 @@ kernels.  There is no fallback: if the library is missing, every call
 raises.
 
 Pool layout (see include/pa.h):
-  k_cache [num_blocks, Hkv, 16, D] bf16,  v_cache [num_blocks, Hkv, D, 16] bf16.
+  k_cache [num_blocks, Hkv, D/32, 16, 32] bf16 (element d of the K row of
+  in-block offset o at [b, g, d // 32, o, d % 32]),
+  v_cache [num_blocks, Hkv, D, 16] bf16.
 """
 from __future__ import annotations
 
@@ -154,12 +156,13 @@ def _on_gpu(*tensors):
 
 
 def _pools(k_cache, v_cache):
-    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(k_cache, "k_cache", torch.bfloat16, 5)
     _need(v_cache, "v_cache", torch.bfloat16, 4)
-    nb, hkv, bs, d = k_cache.shape
-    if bs != BLOCK_SIZE or tuple(v_cache.shape) != (nb, hkv, d, BLOCK_SIZE):
-        raise ValueError("pools must be K [NB, Hkv, 16, D] and V [NB, Hkv, D, 16]; got "
-                         f"{tuple(k_cache.shape)} and {tuple(v_cache.shape)}")
+    nb, hkv, ns, bs, w = k_cache.shape
+    d = ns * w
+    if bs != BLOCK_SIZE or w != 32 or tuple(v_cache.shape) != (nb, hkv, d, BLOCK_SIZE):
+        raise ValueError("pools must be K [NB, Hkv, D/32, 16, 32] and V [NB, Hkv, D, 16]; "
+                         f"got {tuple(k_cache.shape)} and {tuple(v_cache.shape)}")
     return nb, hkv, d
 
 
@@ -555,14 +558,16 @@ def copy_blocks(dst_k, dst_v, src_k, src_v, dst_ids=None, src_ids=None, num_copi
     pool or pinned host memory in the pool layout.  Runs on the current
     stream of the GPU in use."""
     for t, n in ((dst_k, "dst_k"), (src_k, "src_k")):
-        _reachable(t, n, torch.bfloat16, 4)
+        _reachable(t, n, torch.bfloat16, 5)
     for t, n in ((dst_v, "dst_v"), (src_v, "src_v")):
         _reachable(t, n, torch.bfloat16, 4)
-    dnb, hkv, bs, d = dst_k.shape
+    dnb, hkv, ns, bs, w = dst_k.shape
+    d = ns * w
     snb = src_k.shape[0]
-    if bs != BLOCK_SIZE or tuple(src_k.shape[1:]) != (hkv, bs, d) \
+    if bs != BLOCK_SIZE or w != 32 or tuple(src_k.shape[1:]) != (hkv, ns, bs, w) \
             or tuple(dst_v.shape) != (dnb, hkv, d, bs) or tuple(src_v.shape) != (snb, hkv, d, bs):
-        raise ValueError("pools must be K [NB, Hkv, 16, D] and V [NB, Hkv, D, 16] on both sides")
+        raise ValueError("pools must be K [NB, Hkv, D/32, 16, 32] and V [NB, Hkv, D, 16] "
+                         "on both sides")
     for t, n in ((dst_ids, "dst_ids"), (src_ids, "src_ids")):
         if t is not None:
             _reachable(t, n, torch.int32, 1)

@@ -63,15 +63,19 @@ __device__ __forceinline__ void load_pair(PairRegs<D>& r, const uint16_t* __rest
                                           int64_t physy, int g, int hkv, int col, int c) {
   // K: score-tile row `col` -> key: group gr = col/4 picks the block (gr >= 2
   // -> second block) and the 4-key run 8*(gr&1) (+4 for the second tile).
+  // The pool keeps each 32-wide slice i of the head dimension as the block's
+  // 16 keys in 64-byte rows, so for k-step i a 4-key run is 256 contiguous
+  // bytes and every load instruction covers whole 128-byte lines.
   {
     const int gr = col >> 2;
     const int key = 8 * (gr & 1) + (col & 3);
     const int64_t phys = gr >= 2 ? physy : physx;
-    const uint16_t* base = k_cache + ((phys * hkv + g) * kBlock + key) * D + 8 * c;
+    const uint16_t* base = k_cache + (phys * hkv + g) * kBlock * D + key * 32 + 8 * c;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int i = 0; i < D / 32; ++i) r.k[t][i] = load16_stream(base + t * 4 * D + 32 * i);
+      for (int i = 0; i < D / 32; ++i)
+        r.k[t][i] = load16_stream(base + t * 4 * 32 + i * 32 * kBlock);
   }
   // V^T: lane group c reads keys 8*(c&1)..+8 of block (c >= 2 ? y : x), for
   // d row 16*dt + col.
@@ -206,9 +210,9 @@ __device__ __forceinline__ void store_new_row(uint16_t* k_pool, uint16_t* v_pool
                                               const uint32_t (&newv)[D / 16], int64_t tile,
                                               int off, int col, int c) {
   if (col == 0) {
-    uint16_t* kd = k_pool + (tile * kBlock + off) * D + 8 * c;
+    uint16_t* kd = k_pool + tile * kBlock * D + off * 32 + 8 * c;
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) *reinterpret_cast<u32x4*>(kd + 32 * i) = newk[i];
+    for (int i = 0; i < D / 32; ++i) *reinterpret_cast<u32x4*>(kd + i * 32 * kBlock) = newk[i];
   }
   if (c == 0) {
     uint16_t* vd = v_pool + (tile * D + col) * kBlock + off;
@@ -251,10 +255,11 @@ __device__ __forceinline__ void store_new_row_lds(uint16_t* k_pool, uint16_t* v_
                                                   const uint16_t* kr, const uint16_t* vr,
                                                   int64_t tile, int off, int col, int c) {
   if (col == 0) {
-    uint16_t* kd = k_pool + (tile * kBlock + off) * D + 8 * c;
+    uint16_t* kd = k_pool + tile * kBlock * D + off * 32 + 8 * c;
 #pragma unroll
     for (int i = 0; i < D / 32; ++i)
-      *reinterpret_cast<u32x4*>(kd + 32 * i) = *reinterpret_cast<const u32x4*>(kr + 8 * c + 32 * i);
+      *reinterpret_cast<u32x4*>(kd + i * 32 * kBlock) =
+          *reinterpret_cast<const u32x4*>(kr + 8 * c + 32 * i);
   }
   if (c == 0) {
     uint16_t* vd = v_pool + (tile * D + col) * kBlock + off;

@@ -24,7 +24,8 @@
 // (lane/4 % 8) have the same bit parity, e.g. lanes 0-3, 12-15, 20-23, 24-27
 // (measured with the bank-conflict counter).  The layouts give each such
 // group 16 different 16-byte bank slots:
-//   K tile   [BK keys][D], row r chunk j stored at chunk j ^ kswz(r)
+//   K tile   [BK keys][D], row r chunk j stored at chunk j ^ kswz(r) (the
+//            pool's 32-wide slices are put back together into rows)
 //   V^T tile [BK/16 blocks][D rows][16 keys], as in the pool (one contiguous
 //            HBM read per copy)
 //
@@ -342,8 +343,12 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_kernel(
       const int off = 16 * lane;
       const int r = r0 + off / (2 * D);
       const int j = ((off % (2 * D)) / 16) ^ kswz<D>(r);
-      __builtin_amdgcn_global_load_lds(kt + (uint32_t)((r & 15) * D + 8 * j), sb + 1024 * m,
-                                       16, 0, 0);
+      // Chunk j of key row r sits in the pool's 32-wide slice j/4, as the
+      // (j%4)-th 16 bytes of that slice's 64-byte row r: one copy takes the
+      // same kRowsPer rows of every slice, whole 128-byte lines.
+      __builtin_amdgcn_global_load_lds(
+          kt + (uint32_t)((j >> 2) * 32 * kBlock + (r & 15) * 32 + 8 * (j & 3)), sb + 1024 * m,
+          16, 0, 0);
     }
 #pragma unroll
     for (int k = 0; k < VPW; ++k) {

@@ -2,8 +2,9 @@
 //
 // One workgroup handles 16 consecutive new tokens of one KV head.  Thread
 // (t, j) = (tid / 16, tid % 16) owns token t and the j-th sixteenth of the
-// head dimension, so 16 consecutive lanes read (and, for K, write) one
-// token's contiguous row.  When the 16 tokens fill one block in order (every
+// head dimension, so 16 consecutive lanes read one token's contiguous row.
+// A sixteenth never straddles a 32-wide slice of the K pool, so each thread's
+// K piece is contiguous there too (slice d0/32, row `offset`).  When the 16 tokens fill one block in order (every
 // full block of a prefill), the workgroup stages the V rows in LDS and
 // stores the block's transposed V^T tile in 16-byte pieces; otherwise each
 // V element is stored at its (d, offset) place on its own.
@@ -44,8 +45,9 @@ __global__ __launch_bounds__(256) void write_kv_kernel(
   const int64_t src = ((int64_t)t * num_kv_heads + g) * D + d0;
   const int64_t tile = (blk * num_kv_heads + g);
 
-  // K: the piece of the token's row, contiguous in k_new and in the pool.
-  uint16_t* kdst = k_cache + (tile * kBlock + off) * D + d0;
+  // K: the piece of the token's row, contiguous in k_new and in its slice
+  // of the pool (element d at ((tile*D/32 + d/32)*16 + off)*32 + d%32).
+  uint16_t* kdst = k_cache + tile * kBlock * D + (d0 / 32) * 32 * kBlock + off * 32 + (d0 % 32);
   if constexpr (EPT == 4) {
     *reinterpret_cast<u32x2*>(kdst) = *reinterpret_cast<const u32x2*>(k_new + src);
   } else {

@@ -1,9 +1,12 @@
 """Shared test-side helpers: tensor <-> numpy bit views and a test-side
 builder that scatters logical per-sequence K/V into the pool layout.
 
-The pool layout is the library contract: K [NB, Hkv, 16, D] and
+The pool layout is the library contract: K [NB, Hkv, D/32, 16, 32] (element
+d of the K row of in-block offset o at [b, g, d // 32, o, d % 32]) and
 V [NB, Hkv, D, 16] (bf16), token p of a sequence at physical block
-block_table[p // 16], offset p % 16.
+block_table[p // 16], offset p % 16.  Tiny oracle-only cases whose D is not a
+multiple of 32 use one K slice of width D ([NB, Hkv, 1, 16, D]); the oracle
+takes the slice width from the pool's last axis.
 """
 import numpy as np
 import torch
@@ -36,6 +39,25 @@ def random_bf16_bits(gen: torch.Generator, shape, sigma=1.0) -> np.ndarray:
     return bits(x.to(torch.bfloat16))
 
 
+def k_slice_width(d: int) -> int:
+    """Width of a K pool slice: 32 (the library's) or, for D not a multiple
+    of 32, D itself."""
+    return 32 if d % 32 == 0 else d
+
+
+def k_pool_from_rows(rows: np.ndarray) -> np.ndarray:
+    """Token rows [..., 16, D] -> K pool layout [..., D/W, 16, W]."""
+    *lead, bs, d = rows.shape
+    w = k_slice_width(d)
+    return np.ascontiguousarray(np.moveaxis(rows.reshape(*lead, bs, d // w, w), -2, -3))
+
+
+def k_rows_of_pool(pool: np.ndarray) -> np.ndarray:
+    """K pool [..., D/W, 16, W] -> token rows [..., 16, D]."""
+    *lead, ns, bs, w = pool.shape
+    return np.ascontiguousarray(np.moveaxis(pool, -3, -2).reshape(*lead, bs, ns * w))
+
+
 def scatter_to_pool(keys_bits, values_bits, block_table, num_blocks, fill=NAN_BITS):
     """Build K/V pools from logical per-sequence K/V.
 
@@ -44,14 +66,16 @@ def scatter_to_pool(keys_bits, values_bits, block_table, num_blocks, fill=NAN_BI
     Every other slot holds `fill` (NaN by default).
     """
     hkv, d = keys_bits[0].shape[1], keys_bits[0].shape[2]
-    kc = np.full((num_blocks, hkv, BLOCK, d), fill, dtype=np.uint16)
+    w = k_slice_width(d)
+    kc = np.full((num_blocks, hkv, d // w, BLOCK, w), fill, dtype=np.uint16)
     vc = np.full((num_blocks, hkv, d, BLOCK), fill, dtype=np.uint16)
     for s, (ks, vs) in enumerate(zip(keys_bits, values_bits)):
         for p in range(ks.shape[0]):
             b = int(block_table[s][p // BLOCK])
             o = p % BLOCK
             for g in range(hkv):
-                kc[b, g, o, :] = ks[p, g]
+                for j in range(d // w):
+                    kc[b, g, j, o, :] = ks[p, g, j * w:(j + 1) * w]
                 vc[b, g, :, o] = vs[p, g]
     return kc, vc
 

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 from _helpers import (bits, exact_bf16_bits, padded_table, random_bf16_bits,
-                      scatter_to_pool)
+                      scatter_to_pool, k_pool_from_rows)
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
                       "closed_form_cases.json")
@@ -220,24 +220,31 @@ def pin_brute_partials():
 
 
 def pin_write_kv_elementwise():
+    """Element by element from the layout contract: K element i of the token
+    in slot (b, o) lands at [b, g, i // W, o, i % W] (W = slice width: one
+    slice for D = 5, two 32-wide slices for D = 64), V element i at
+    [b, g, i, o]."""
     gen = torch.Generator().manual_seed(3)
-    nb, hkv, d, T = 6, 3, 5, 9
-    kc = random_bf16_bits(gen, (nb, hkv, 16, d))
-    vc = random_bf16_bits(gen, (nb, hkv, d, 16))
-    kn = random_bf16_bits(gen, (T, hkv, d))
-    vn = random_bf16_bits(gen, (T, hkv, d))
-    slots = np.array([0, 17, 95, -1, 40, 16 * 5 + 15, 33, -7, 2], dtype=np.int64)
-    k2, v2 = oracle.write_kv(kc, vc, kn, vn, slots)
-    ek, ev = kc.copy(), vc.copy()
-    for t in range(T):
-        if slots[t] < 0:
-            continue
-        for g in range(hkv):
-            for i in range(d):
-                ek[slots[t] // 16, g, slots[t] % 16, i] = kn[t, g, i]
-                ev[slots[t] // 16, g, i, slots[t] % 16] = vn[t, g, i]
-    assert np.array_equal(k2, ek) and np.array_equal(v2, ev)
-    assert k2.dtype == np.uint16 and v2.dtype == np.uint16
+    for d in (5, 64):
+        nb, hkv, T = 6, 3, 9
+        w = 32 if d == 64 else d
+        kc = k_pool_from_rows(random_bf16_bits(gen, (nb, hkv, 16, d)))
+        assert kc.shape == (nb, hkv, d // w, 16, w)
+        vc = random_bf16_bits(gen, (nb, hkv, d, 16))
+        kn = random_bf16_bits(gen, (T, hkv, d))
+        vn = random_bf16_bits(gen, (T, hkv, d))
+        slots = np.array([0, 17, 95, -1, 40, 16 * 5 + 15, 33, -7, 2], dtype=np.int64)
+        k2, v2 = oracle.write_kv(kc, vc, kn, vn, slots)
+        ek, ev = kc.copy(), vc.copy()
+        for t in range(T):
+            if slots[t] < 0:
+                continue
+            for g in range(hkv):
+                for i in range(d):
+                    ek[slots[t] // 16, g, i // w, slots[t] % 16, i % w] = kn[t, g, i]
+                    ev[slots[t] // 16, g, i, slots[t] % 16] = vn[t, g, i]
+        assert np.array_equal(k2, ek) and np.array_equal(v2, ev)
+        assert k2.dtype == np.uint16 and v2.dtype == np.uint16
 
 
 # ---------------------------------------------------------------------------
@@ -245,8 +252,16 @@ def pin_write_kv_elementwise():
 # ---------------------------------------------------------------------------
 
 def pin_closed_forms():
+    """Single key, identical keys, zero query and two keys (sigmoid weights),
+    at D = 8 (one K slice) and D = 64 (two 32-wide slices, so a slice read
+    out of order changes the two-key scores)."""
     gen = torch.Generator().manual_seed(11)
-    hq, hkv, d = 4, 2, 8
+    for d in (8, 64):
+        _closed_forms_at(gen, d)
+
+
+def _closed_forms_at(gen, d):
+    hq, hkv = 4, 2
     # single token: output is V exactly
     bt, kc, vc, K, V = _tiny_paged(gen, [1, 1], hq, hkv, d)
     q = random_bf16_bits(gen, (2, hq, d))
@@ -258,9 +273,9 @@ def pin_closed_forms():
     lens = [23]
     bt, kc, vc, K, V = _tiny_paged(gen, lens, hq, hkv, d)
     kc_same = kc.copy()
-    row = kc[bt[0][0], :, 0, :].copy()
+    row = kc[bt[0][0], :, :, 0, :].copy()
     for p in range(23):
-        kc_same[bt[0][p // 16], :, p % 16, :] = row
+        kc_same[bt[0][p // 16], :, :, p % 16, :] = row
     out = oracle.decode(q[:1], kc_same, vc, bt, lens, 0.7, hq, hkv)
     for h in range(hq):
         assert np.allclose(out[0, h], V[0][:, h // 2].mean(axis=0), rtol=1e-13, atol=1e-14)
@@ -326,7 +341,8 @@ def pin_poison_ignored():
     # token's slot too; restore it)
     kb, vb = bits(b.k_cache), bits(b.v_cache)
     ka, va = bits(a.k_cache), bits(a.v_cache)
-    kb, vb = oracle.write_kv(kb, vb, np.stack([ka[s // 16, :, s % 16, :] for s in a.slot_mapping.numpy()]),
+    kb, vb = oracle.write_kv(kb, vb, np.stack([ka[s // 16, :, :, s % 16, :].reshape(2, -1)
+                                       for s in a.slot_mapping.numpy()]),
                              np.stack([va[s // 16, :, :, s % 16] for s in a.slot_mapping.numpy()]),
                              a.slot_mapping.numpy())
     assert np.isnan(oracle.bf16_bits_to_f64(kb)).any()
@@ -356,7 +372,7 @@ def pin_causal_perturbation_and_prefill_vs_decode():
     kc2, vc2 = kc.copy(), vc.copy()
     for p in range(pl[s] + i + 1, pl[s] + c.q_lens[s]):
         b, o = bt[s, p // 16], p % 16
-        kc2[b, :, o, :] ^= np.uint16(0x0040)
+        kc2[b, :, :, o, :] ^= np.uint16(0x0040)
         vc2[b, :, :, o] ^= np.uint16(0x0040)
     pert = oracle.prefill(q, kc2, vc2, bt, cu, pl, c.scale, 4, 2)
     rows = slice(cu[s], cu[s] + i + 1)
@@ -427,10 +443,10 @@ def pin_closed_forms_decode_multi():
     hq, hkv, d, T = 4, 2, 8, 6
     lens = [6, 29]
     bt, kc, vc, K, V = _tiny_paged(gen, lens, hq, hkv, d)
-    row = kc[bt[0][0], :, 0, :].copy()
+    row = kc[bt[0][0], :, :, 0, :].copy()
     for s, L in enumerate(lens):
         for p in range(L):
-            kc[bt[s][p // 16], :, p % 16, :] = row
+            kc[bt[s][p // 16], :, :, p % 16, :] = row
     q = random_bf16_bits(gen, (2, T, hq, d))
     out = oracle.decode_multi(q, kc, vc, bt, lens, 0.8, hq, hkv)
     for s, L in enumerate(lens):
@@ -491,9 +507,9 @@ def pin_copy_blocks_elementwise():
     untouched blocks keep their bits; None ids mean blocks 0..n-1."""
     gen = torch.Generator().manual_seed(61)
     hkv, d = 3, 5
-    sk = random_bf16_bits(gen, (7, hkv, 16, d))
+    sk = k_pool_from_rows(random_bf16_bits(gen, (7, hkv, 16, d)))
     sv = random_bf16_bits(gen, (7, hkv, d, 16))
-    dk0 = random_bf16_bits(gen, (9, hkv, 16, d))
+    dk0 = k_pool_from_rows(random_bf16_bits(gen, (9, hkv, 16, d)))
     dv0 = random_bf16_bits(gen, (9, hkv, d, 16))
     src = np.array([6, 0, 3, 9, 2, -1], dtype=np.int32)
     dst = np.array([1, 8, 4, 2, 12, 5], dtype=np.int32)
@@ -505,11 +521,11 @@ def pin_copy_blocks_elementwise():
         for g in range(hkv):
             for r in range(16):
                 for e in range(d):
-                    ek[dst[i], g, r, e] = sk[src[i], g, r, e]
+                    ek[dst[i], g, 0, r, e] = sk[src[i], g, 0, r, e]
                     ev[dst[i], g, e, r] = sv[src[i], g, e, r]
     assert np.array_equal(dk, ek) and np.array_equal(dv, ev)
     assert np.array_equal(dk[[0, 2, 3, 5, 6, 7]], dk0[[0, 2, 3, 5, 6, 7]])
-    pk, pv = oracle.copy_blocks(np.zeros((3, hkv, 16, d), np.uint16),
+    pk, pv = oracle.copy_blocks(np.zeros((3, hkv, 1, 16, d), np.uint16),
                                 np.zeros((3, hkv, d, 16), np.uint16), None, sk, sv,
                                 np.array([5, 1, 4], dtype=np.int32), 3)
     assert np.array_equal(pk, sk[[5, 1, 4]]) and np.array_equal(pv, sv[[5, 1, 4]])

@@ -15,7 +15,7 @@ BF, F32, I32 = torch.bfloat16, torch.float32, torch.int32
 
 
 def pools():
-    return (torch.zeros(NB, HKV, 16, D, dtype=BF), torch.zeros(NB, HKV, D, 16, dtype=BF))
+    return (torch.zeros(NB, HKV, D // 32, 16, 32, dtype=BF), torch.zeros(NB, HKV, D, 16, dtype=BF))
 
 
 def inputs(T=None):
@@ -31,6 +31,22 @@ def reaches_device_check(fn):
 def rejects(fn, name):
     with pytest.raises((ValueError, TypeError), match=name):
         fn()
+
+
+def test_pool_layout_checked():
+    """K must be [NB, Hkv, D/32, 16, 32]: the token-row shape [NB, Hkv, 16, D],
+    another slice width, or a K/V head-dim mismatch is refused."""
+    kc, vc = pools()
+    q, bt, ctx = inputs()
+    call = lambda k, v: pa.decode(q, k, v, bt, ctx, 0.1, partition_size=64,  # noqa: E731
+                                  num_partitions=1)
+    reaches_device_check(lambda: call(kc, vc))
+    rejects(lambda: call(torch.zeros(NB, HKV, 16, D, dtype=BF), vc), "k_cache")
+    rejects(lambda: call(torch.zeros(NB, HKV, D // 16, 16, 16, dtype=BF), vc), "pools")
+    rejects(lambda: call(torch.zeros(NB, HKV, D // 32 + 1, 16, 32, dtype=BF), vc), "pools")
+    kn = torch.zeros(B, HKV, D, dtype=BF)
+    rejects(lambda: pa.write_kv(kn, kn, torch.zeros(B, dtype=torch.int64),
+                                torch.zeros(NB, HKV, 16, D, dtype=BF), vc), "k_cache")
 
 
 def test_decode_single_partition_out_shape():

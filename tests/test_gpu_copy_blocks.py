@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _pool(gen, nb, hkv, d):
-    return (from_bits(random_bf16_bits(gen, (nb, hkv, 16, d))),
+    return (from_bits(random_bf16_bits(gen, (nb, hkv, d // 32, 16, 32))),
             from_bits(random_bf16_bits(gen, (nb, hkv, d, 16))))
 
 
@@ -77,11 +77,11 @@ def test_save_to_pinned_host_buffer():
     hkv, d, n, nb = 2, 256, 21, 40
     k, v = _pool(gen, nb, hkv, d)
     src = torch.randperm(nb, generator=gen)[:n].tolist()
-    host_k = torch.zeros((n, hkv, 16, d), dtype=torch.bfloat16, pin_memory=True)
+    host_k = torch.zeros((n, hkv, d // 32, 16, 32), dtype=torch.bfloat16, pin_memory=True)
     host_v = torch.zeros((n, hkv, d, 16), dtype=torch.bfloat16, pin_memory=True)
     pa.copy_blocks(host_k, host_v, k.to(DEV), v.to(DEV), src_ids=_ids(src).to(DEV))
     torch.cuda.synchronize()
-    ek, ev = oracle.copy_blocks(np.zeros((n, hkv, 16, d), np.uint16),
+    ek, ev = oracle.copy_blocks(np.zeros((n, hkv, d // 32, 16, 32), np.uint16),
                                 np.zeros((n, hkv, d, 16), np.uint16), None, bits(k), bits(v),
                                 np.array(src), n)
     assert np.array_equal(bits(host_k), ek) and np.array_equal(bits(host_v), ev)
@@ -102,13 +102,13 @@ def test_restored_blocks_decode_identically():
     args = (case.q.to(DEV),)
     base = pa.decode(*args, kc, vc, bt.to(DEV), case.context_lens.to(DEV), case.scale,
                      partition_size=128)
-    host_k = torch.empty((n, 8, 16, 128), dtype=torch.bfloat16, pin_memory=True)
+    host_k = torch.empty((n, 8, 4, 16, 32), dtype=torch.bfloat16, pin_memory=True)
     host_v = torch.empty((n, 8, 128, 16), dtype=torch.bfloat16, pin_memory=True)
     pa.copy_blocks(host_k, host_v, kc, vc, src_ids=_ids(used).to(DEV))
     gen = torch.Generator().manual_seed(31)
     nb2 = 400
     fresh = torch.randperm(nb2, generator=gen)[:n]
-    k2 = torch.randn((nb2, 8, 16, 128), generator=gen).to(torch.bfloat16).to(DEV)
+    k2 = torch.randn((nb2, 8, 4, 16, 32), generator=gen).to(torch.bfloat16).to(DEV)
     v2 = torch.randn((nb2, 8, 128, 16), generator=gen).to(torch.bfloat16).to(DEV)
     pa.copy_blocks(k2, v2, host_k, host_v, dst_ids=fresh.to(torch.int32).to(DEV))
     remap = dict(zip(used, fresh.tolist()))

@@ -32,7 +32,7 @@ assert HIGH_BASE * HKV * 16 * D > 2**31 and HIGH_BASE * HKV * 16 * D * 2 > 2**32
 @pytest.fixture(scope="module")
 def large_pools():
     announce(f"large pools: 2 x {LARGE_BLOCKS} blocks x {HKV * 16 * D * 2} B")
-    k = torch.empty((LARGE_BLOCKS, HKV, 16, D), dtype=torch.bfloat16, device=DEV)
+    k = torch.empty((LARGE_BLOCKS, HKV, D // 32, 16, 32), dtype=torch.bfloat16, device=DEV)
     v = torch.empty((LARGE_BLOCKS, HKV, D, 16), dtype=torch.bfloat16, device=DEV)
     yield k, v
     del k, v
@@ -200,7 +200,7 @@ def test_large_pool_copy_blocks(large_pools):
     announce("large pool copy_blocks")
     gen = torch.Generator().manual_seed(75)
     nb = 48
-    kc = workloads._normal_bf16(gen, (nb, HKV, 16, D), 1.0)
+    kc = workloads._normal_bf16(gen, (nb, HKV, D // 32, 16, 32), 1.0)
     vc = workloads._normal_bf16(gen, (nb, HKV, D, 16), 1.0)
     ids = _high_ids(nb, 9)
     bk, bv = _place(large_pools, kc, vc, ids)

@@ -45,7 +45,7 @@ def test_write_kv_random_slots_skips_negative_and_out_of_range(d):
     announce(f"write_kv random slots d={d}")
     g = torch.Generator().manual_seed(d)
     nb, hkv, T = 37, 3, 300
-    k0 = torch.randn(nb, hkv, 16, d, generator=g).to(torch.bfloat16)
+    k0 = torch.randn(nb, hkv, d // 32, 16, 32, generator=g).to(torch.bfloat16)
     v0 = torch.randn(nb, hkv, d, 16, generator=g).to(torch.bfloat16)
     kn = torch.randn(T, hkv, d, generator=g).to(torch.bfloat16)
     vn = torch.randn(T, hkv, d, generator=g).to(torch.bfloat16)
@@ -62,7 +62,7 @@ def test_write_kv_random_slots_skips_negative_and_out_of_range(d):
 
 
 def test_write_kv_zero_tokens_is_noop():
-    kc = torch.zeros(2, 1, 16, 64, dtype=torch.bfloat16, device=DEV)
+    kc = torch.zeros(2, 1, 2, 16, 32, dtype=torch.bfloat16, device=DEV)
     vc = torch.zeros(2, 1, 64, 16, dtype=torch.bfloat16, device=DEV)
     e = torch.empty(0, 1, 64, dtype=torch.bfloat16, device=DEV)
     pa.write_kv(e, e, torch.empty(0, dtype=torch.int64, device=DEV), kc, vc)
@@ -91,7 +91,7 @@ def test_write_kv_whole_blocks_and_broken_runs(d):
     slots = torch.cat(runs).to(torch.int64)
     slots[3 * 16 + 7] = -1 - 16 * 10                   # the -1 inside run 4, kept negative
     T = slots.numel()
-    k0 = torch.randn(nb, hkv, 16, d, generator=g).to(torch.bfloat16)
+    k0 = torch.randn(nb, hkv, d // 32, 16, 32, generator=g).to(torch.bfloat16)
     v0 = torch.randn(nb, hkv, d, 16, generator=g).to(torch.bfloat16)
     kn = torch.randn(T, hkv, d, generator=g).to(torch.bfloat16)
     vn = torch.randn(T, hkv, d, generator=g).to(torch.bfloat16)

@@ -17,8 +17,12 @@ MUTATIONS = {
                              "return h % num_kv_heads"),
     "offset_off_by_one": ("return int(block_table_row[pos // BLOCK]), pos % BLOCK",
                           "return int(block_table_row[pos // BLOCK]), (pos + 1) % BLOCK"),
-    "k_reversed_dims": ("return k_cache[block, :, off, :]",
-                        "return k_cache[block, :, off, ::-1]"),
+    "k_reversed_dims": ("return k_cache[block, :, :, off, :].reshape(hkv, -1)",
+                        "return k_cache[block, :, :, off, ::-1].reshape(hkv, -1)"),
+    "k_slices_reversed": ("return k_cache[block, :, :, off, :].reshape(hkv, -1)",
+                          "return k_cache[block, :, ::-1, off, :].reshape(hkv, -1)"),
+    "k_slice_major_read": ("return k_cache[block, :, :, off, :].reshape(hkv, -1)",
+                           "return k_cache[block, :, :, off, :].swapaxes(1, 2).reshape(hkv, -1)"),
     "v_reversed_dims": ("return v_cache[block, :, :, off]",
                         "return v_cache[block, :, :, off][:, ::-1]"),
     "slot_block_offset_swapped": ("return slot // BLOCK, slot % BLOCK",
@@ -34,7 +38,11 @@ MUTATIONS = {
                         "part_lse[s, h, p] = np.log(np.sum(e))"),
     "combine_weight_sign": ("w = np.exp(lse - M)", "w = np.exp(M - lse)"),
     "bf16_widen_shift": ("<< np.uint32(16)", "<< np.uint32(15)"),
-    "write_k_from_v": ("kc[b, :, o, :] = k_new[t]", "kc[b, :, o, :] = v_new[t]"),
+    "write_k_from_v": ("kc[b, :, :, o, :] = np.asarray(k_new[t])",
+                       "kc[b, :, :, o, :] = np.asarray(v_new[t])"),
+    "write_k_slice_major": (
+        "kc[b, :, :, o, :] = np.asarray(k_new[t]).reshape(kc.shape[1], kc.shape[2], kc.shape[4])",
+        "kc[b, :, :, o, :] = np.asarray(k_new[t]).reshape(kc.shape[1], kc.shape[4], kc.shape[2]).swapaxes(1, 2)"),
     "decode_excludes_self": ("np.array([n]),", "np.array([n - 1]),"),
     "partitions_overlap": ("lo, hi = p * partition_size, min(n, (p + 1) * partition_size)",
                            "lo, hi = p * partition_size, min(n, (p + 1) * partition_size + 1)"),
@@ -48,7 +56,7 @@ MUTATIONS = {
     "multi_short_context_not_nan": ("            out[s] = np.nan\n", "            pass\n"),
     "copy_ids_swapped": ("s = i if src_ids is None else int(src_ids[i])\n        d = i if dst_ids is None else int(dst_ids[i])",
                          "d = i if src_ids is None else int(src_ids[i])\n        s = i if dst_ids is None else int(dst_ids[i])"),
-    "copy_v_from_k": ("dv[d] = src_v[s]", "dv[d] = np.swapaxes(src_k[s], 1, 2)"),
+    "copy_v_dst_index": ("dv[d] = src_v[s]", "dv[d] = src_v[d % src_v.shape[0]]"),
     "copy_skip_check_dropped": ("if not (0 <= s < src_k.shape[0] and 0 <= d < dk.shape[0]):",
                                 "if not (-src_k.shape[0] <= s < src_k.shape[0] and 0 <= d < dk.shape[0]):"),
     "prefix_key_ignores_earlier_blocks": (
@@ -78,15 +86,18 @@ def _mutant(path, old, new):
 
 
 def _mutated_oracle(spec):
-    """The oracle package with one of its modules replaced by a mutant."""
+    """The oracle package with one of its modules replaced by a mutant: every
+    name the package exports, the mutant's definitions taking precedence, so
+    a pin that exercises another module still runs (and a survivor is not
+    counted as caught through a missing name)."""
     import oracle
     path, old, new = spec if len(spec) == 3 else (SRC, *spec)
     mod = _mutant(path, old, new)
-    if path == SRC:
-        return mod
     ns = types.SimpleNamespace(**{k: getattr(oracle, k) for k in dir(oracle)
                                   if not k.startswith("__")})
-    ns.PrefixCache = mod.PrefixCache
+    for k in dir(mod):
+        if not k.startswith("__"):
+            setattr(ns, k, getattr(mod, k))
     return ns
 
 

@@ -49,7 +49,7 @@ def test_noalloc_one_partition_and_split_small_batch():
 def test_noalloc_rejects_pieces_beyond_the_scratch():
     # 64 sequences x 64 heads x 8 partitions x (128 + 1) floats = 16.1 MiB
     announce("decode_noalloc too large")
-    kc = torch.zeros(16, 8, 16, 128, dtype=torch.bfloat16, device=DEV)
+    kc = torch.zeros(16, 8, 4, 16, 32, dtype=torch.bfloat16, device=DEV)
     vc = torch.zeros(16, 8, 128, 16, dtype=torch.bfloat16, device=DEV)
     q = torch.zeros(64, 64, 128, dtype=torch.bfloat16, device=DEV)
     bt = torch.zeros(64, 1, dtype=torch.int32, device=DEV)

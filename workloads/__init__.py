@@ -11,15 +11,19 @@ with 128-token outputs in the serving-load tables; up to 64 requests in
 flight; 4097- and 8192-token long prompts on "Qwen3.5-4B / 9B / 27B").
 
 Pool layout (shared contract of the whole library):
-  K pool  [num_blocks, Hkv, 16, D]  bf16  (token rows of D contiguous values)
+  K pool  [num_blocks, Hkv, D/32, 16, 32]  bf16  (per 32-wide slice of the
+          head dimension, 16 token rows of 32 contiguous values)
   V pool  [num_blocks, Hkv, D, 16]  bf16  (transposed: 16 token values per d)
-A token at logical position p of sequence s lives in physical block
+Element d of the K row of the token at in-block offset o sits at
+k_cache[block, head, d // 32, o, d % 32].  A token at logical position p of sequence s lives in physical block
 block_tables[s, p // 16], at in-block offset p % 16; its slot id is
 block * 16 + offset.
 
 Draw order (fixed, generator torch.Generator('cpu') seeded with 42 by
 default): lengths -> block permutation -> K pool -> V pool -> Q -> new-token
-K/V.  Normals are drawn in fp32, multiplied by sigma and rounded to bf16.
+K/V.  Normals are drawn in fp32, multiplied by sigma and rounded to bf16.  The
+K pool is drawn in token-row order [num_blocks, Hkv, 16, D] and then stored in
+the sliced layout above, so a given seed fixes the same K row for every token.
 """
 from __future__ import annotations
 
@@ -42,7 +46,7 @@ class DecodeCase:
     scale: float
     context_lens: torch.Tensor      # int32 [B]; includes the token being decoded
     block_tables: torch.Tensor      # int32 [B, max_blocks]; padding = -1
-    k_cache: torch.Tensor           # bf16 [NB, Hkv, 16, D]
+    k_cache: torch.Tensor           # bf16 [NB, Hkv, D/32, 16, 32]
     v_cache: torch.Tensor           # bf16 [NB, Hkv, D, 16]
     q: torch.Tensor                 # bf16 [B, Hq, D]
     k_new: torch.Tensor             # bf16 [B, Hkv, D]  K of the decoded token
@@ -77,7 +81,7 @@ class PrefillCase:
     cu_seqlens: torch.Tensor        # int32 [S+1] over new tokens
     prefix_lens: torch.Tensor       # int32 [S]
     block_tables: torch.Tensor      # int32 [S, max_blocks]; padding = -1
-    k_cache: torch.Tensor           # bf16 [NB, Hkv, 16, D]; prefix tokens live
+    k_cache: torch.Tensor           # bf16 [NB, Hkv, D/32, 16, 32]; prefix tokens live
     v_cache: torch.Tensor           # bf16 [NB, Hkv, D, 16]
     q: torch.Tensor                 # bf16 [total_q, Hq, D]
     k_new: torch.Tensor             # bf16 [total_q, Hkv, D]
@@ -116,7 +120,7 @@ class MultiDecodeCase:
     query_len: int
     context_lens: torch.Tensor      # int32 [B]; includes the T query tokens
     block_tables: torch.Tensor      # int32 [B, max_blocks]; padding = -1
-    k_cache: torch.Tensor           # bf16 [NB, Hkv, 16, D]
+    k_cache: torch.Tensor           # bf16 [NB, Hkv, D/32, 16, 32]
     v_cache: torch.Tensor           # bf16 [NB, Hkv, D, 16]
     q: torch.Tensor                 # bf16 [B, T, Hq, D]
     k_new: torch.Tensor             # bf16 [B*T, Hkv, D]  K of the query tokens
@@ -145,6 +149,16 @@ def _normal_bf16(g, shape, sigma, device="cpu"):
     if sigma != 1.0:
         x = x * sigma
     return x.to(torch.bfloat16)
+
+
+def _k_pool(g, num_blocks, num_kv_heads, head_dim, sigma):
+    """K pool drawn as token rows [NB, Hkv, 16, D], stored [NB, Hkv, D/W, 16, W]
+    with slice width W = 32 (head dims that are not a multiple of 32, which
+    only the oracle's own small cases use, get one slice of width D)."""
+    w = 32 if head_dim % 32 == 0 else head_dim
+    rows = _normal_bf16(g, (num_blocks, num_kv_heads, BLOCK_SIZE, head_dim), sigma)
+    return (rows.view(num_blocks, num_kv_heads, BLOCK_SIZE, head_dim // w, w)
+            .permute(0, 1, 3, 2, 4).contiguous())
 
 
 def _assign_blocks(g, num_blocks, blocks_per_seq, max_blocks, permute=True):
@@ -183,7 +197,7 @@ def poison_pool(k_cache, v_cache, block_tables, live_lens):
     kv = k_cache.view(torch.int16)
     vv = v_cache.view(torch.int16)
     nan = torch.tensor(BF16_NAN_BITS, dtype=torch.int32).to(torch.int16)
-    kv[dead.unsqueeze(1).unsqueeze(-1).expand_as(kv)] = nan   # [NB,Hkv,16,D]
+    kv[dead.view(nb, 1, 1, BLOCK_SIZE, 1).expand_as(kv)] = nan  # [NB,Hkv,D/32,16,32]
     vv[dead.unsqueeze(1).unsqueeze(2).expand_as(vv)] = nan    # [NB,Hkv,D,16]
 
 
@@ -201,7 +215,7 @@ def make_decode_case(name, *, context_lens=None, ctx_range=None, batch=None,
     if max_blocks is None:
         max_blocks = max(nblk) if nblk else 1
     bt = _assign_blocks(g, num_blocks, nblk, max_blocks, permute)
-    kc = _normal_bf16(g, (num_blocks, num_kv_heads, BLOCK_SIZE, head_dim), sigma)
+    kc = _k_pool(g, num_blocks, num_kv_heads, head_dim, sigma)
     vc = _normal_bf16(g, (num_blocks, num_kv_heads, head_dim, BLOCK_SIZE), sigma)
     B = int(ctx.numel())
     q = _normal_bf16(g, (B, num_q_heads, head_dim), sigma)
@@ -224,7 +238,7 @@ def decode_layer(case: DecodeCase, seed: int, poison=True) -> DecodeCase:
     seeded with `seed`; draw order K pool -> V pool -> Q -> new-token K/V),
     NaN-poisoned like the original."""
     g = torch.Generator("cpu").manual_seed(seed)
-    kc = _normal_bf16(g, tuple(case.k_cache.shape), case.sigma)
+    kc = _k_pool(g, case.num_blocks, case.num_kv_heads, case.head_dim, case.sigma)
     vc = _normal_bf16(g, tuple(case.v_cache.shape), case.sigma)
     q = _normal_bf16(g, tuple(case.q.shape), case.sigma)
     k_new = _normal_bf16(g, tuple(case.k_new.shape), case.sigma)
@@ -249,7 +263,7 @@ def make_prefill_case(name, *, q_lens, prefix_lens, num_q_heads, num_kv_heads, h
     if max_blocks is None:
         max_blocks = max(nblk) if nblk else 1
     bt = _assign_blocks(g, num_blocks, nblk, max_blocks, permute)
-    kc = _normal_bf16(g, (num_blocks, num_kv_heads, BLOCK_SIZE, head_dim), sigma)
+    kc = _k_pool(g, num_blocks, num_kv_heads, head_dim, sigma)
     vc = _normal_bf16(g, (num_blocks, num_kv_heads, head_dim, BLOCK_SIZE), sigma)
     total_q = sum(q_lens)
     q = _normal_bf16(g, (total_q, num_q_heads, head_dim), sigma)
@@ -287,7 +301,7 @@ def make_multi_decode_case(name, *, query_len, context_lens=None, ctx_range=None
     if max_blocks is None:
         max_blocks = max(nblk) if nblk else 1
     bt = _assign_blocks(g, num_blocks, nblk, max_blocks, permute)
-    kc = _normal_bf16(g, (num_blocks, num_kv_heads, BLOCK_SIZE, head_dim), sigma)
+    kc = _k_pool(g, num_blocks, num_kv_heads, head_dim, sigma)
     vc = _normal_bf16(g, (num_blocks, num_kv_heads, head_dim, BLOCK_SIZE), sigma)
     B = int(ctx.numel())
     q = _normal_bf16(g, (B, T, num_q_heads, head_dim), sigma)
