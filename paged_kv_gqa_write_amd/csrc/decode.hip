@@ -816,7 +816,11 @@ int launch_decode(void* out, float* part_out, float* part_lse, const void* q,
         return 0;
       case 128 * 8 + 4: go(decode_kernel<128, 3, 2, 2, false, C>, 3); return 0;
       case 128 * 8 + 3:
-        if (bpp >= 64) go(decode_kernel<128, 4, 1, 1, true, C>, 4);
+        // The same occupancy rule for the appending form (with the K pool in
+        // 32-wide slices: batch 64 48.61 -> 48.39 us with 2 pairs, 4 x 8192
+        // 24.10 -> 24.28).
+        if (bpp >= 64 && nwg <= kComputeUnits) go(decode_kernel<128, 4, 1, 1, true, C>, 4);
+        else if (bpp >= 64) go(decode_kernel<128, 4, 2, 1, true, C>, 4);
         else go(decode_kernel<128, 3, 2, 1, true, C>, 3);
         return 0;
       case 256 * 8 + 2: go(decode_kernel<256, 4, 2, 1, false, C>, 4); return 0;

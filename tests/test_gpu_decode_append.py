@@ -52,6 +52,18 @@ def test_decode_append_equals_write_then_decode_bitwise(ps):
     assert torch.equal(out, decode_gpu(case, partition_size=ps))
 
 
+@pytest.mark.parametrize("name", ["qwen3_32b_decode_b64", "qwen3_32b_decode_b4_8192",
+                                  "hybrid_decode_b8"])
+def test_decode_append_equals_write_then_decode_bitwise_full_size(name):
+    """The large launches in the library's plan (two workgroups per CU with
+    two pairs in flight, one per CU with one pair, head_dim 256): the
+    appending kernel gives the bits of pa_write_kv + pa_decode."""
+    announce(f"decode_append vs write_kv+decode {name}")
+    case = workloads.DECODE_CASES[name]()
+    out, _, _ = _append_gpu(case)
+    assert torch.equal(out, decode_gpu(case))
+
+
 @pytest.mark.parametrize("hq,hkv,d", [(4, 2, 64), (32, 8, 128), (16, 2, 256), (16, 1, 128)])
 def test_decode_append_new_token_positions(hq, hkv, d):
     """The new token at every kind of place: alone (ctx 1), first and last
@@ -92,6 +104,28 @@ def test_decode_append_long_wave_ranges(hq, hkv, d):
     check_tolerance(f"long wave ranges d={d}", out, ref)
     assert np.array_equal(bits(kc), ek) and np.array_equal(bits(vc), ev)
     assert torch.equal(out, decode_gpu(case, partition_size=8192))
+
+
+def test_decode_two_pairs_in_flight_long_wave_ranges():
+    """264 workgroups (33 sequences x 8 KV heads, one partition of 4736
+    tokens each): more than one per CU, so both forms keep two pairs in
+    flight, and each wave's range of ~37 pairs crosses the table-entry
+    reload after 32.  The new token falls before and after that point
+    depending on the length.  Output against the oracle, pools bit-exact,
+    and the appending kernel bit-identical to pa_write_kv + pa_decode."""
+    announce("decode_append two pairs in flight, long wave ranges")
+    gen = torch.Generator().manual_seed(4736)
+    lens = torch.randint(4100, 4737, (33,), generator=gen).tolist()
+    lens[0], lens[1] = 4736, 4097
+    nb = sum((n + 15) // 16 for n in lens) + 40
+    case = workloads.make_decode_case("twopair", context_lens=lens, num_q_heads=16,
+                                      num_kv_heads=8, head_dim=128, num_blocks=nb, seed=47)
+    ref = decode_oracle(case)
+    ek, ev = _oracle_pools(case)
+    out, kc, vc = _append_gpu(case, partition_size=4736, num_partitions=1)
+    check_tolerance("two pairs in flight", out, ref, literal=True)
+    assert np.array_equal(bits(kc), ek) and np.array_equal(bits(vc), ev)
+    assert torch.equal(out, decode_gpu(case, partition_size=4736, num_partitions=1))
 
 
 def test_decode_append_bad_entry_poisons_and_skips_write():
