@@ -52,12 +52,6 @@ def k_pool_from_rows(rows: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(np.moveaxis(rows.reshape(*lead, bs, d // w, w), -2, -3))
 
 
-def k_rows_of_pool(pool: np.ndarray) -> np.ndarray:
-    """K pool [..., D/W, 16, W] -> token rows [..., 16, D]."""
-    *lead, ns, bs, w = pool.shape
-    return np.ascontiguousarray(np.moveaxis(pool, -3, -2).reshape(*lead, bs, ns * w))
-
-
 def scatter_to_pool(keys_bits, values_bits, block_table, num_blocks, fill=NAN_BITS):
     """Build K/V pools from logical per-sequence K/V.
 
