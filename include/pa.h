@@ -88,7 +88,8 @@ typedef enum {
  * "Qwen3-4B / 8B / 32B", Architecture Notes).
  *
  * For every token t in [0, num_tokens) with slot = slot_mapping[t] >= 0:
- *   K pool row of (slot/16, head g, offset slot%16) := k_new[t, g, :]
+ *   K row of (slot/16, head g, offset slot%16) := k_new[t, g, :]  (its 64-byte
+ *       piece in each of the D/32 slices of the tile, layout above)
  *   V pool column of (slot/16, head g, offset slot%16) := v_new[t, g, :]
  * for all KV heads g.  Pure bit copies (bit-exact).  Slots < 0 are skipped;
  * slots >= num_blocks*16 are invalid and skipped as well (never written).
