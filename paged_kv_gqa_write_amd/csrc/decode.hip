@@ -799,7 +799,9 @@ int launch_decode(void* out, float* part_out, float* part_lse, const void* q,
   // every wave of the launch then waits for the whole first burst (hybrid
   // batch 25.27 -> 24.93 us, 32 x 1024 18.07 -> 16.79, 64 x 512 29.56 ->
   // 28.57, 4 x 16384 27.14 -> 26.70; the plain form loses with 1: 24.71 ->
-  // 26.25 on the hybrid batch).
+  // 26.25 on the hybrid batch).  Re-measured with the K pool in 32-wide
+  // slices, hybrid batch: appending 21.98 (2 pairs) vs 21.16 (1), plain
+  // 21.13 (2) vs 22.34 (1).
   auto pick = [&](auto compact_tag) {
     constexpr bool C = decltype(compact_tag)::value;
     switch (head_dim * 8 + nt * 2 + (append ? 1 : 0)) {
@@ -809,7 +811,9 @@ int launch_decode(void* out, float* part_out, float* part_lse, const void* q,
       case 128 * 8 + 2:
         // Partitions of 32+ pairs: a second pair in flight pays only when two
         // workgroups share a CU (batch 64: 49.31 -> 48.50 us); with one
-        // workgroup per CU one pair is faster (4 x 8192: 25.04 -> 24.44 us).
+        // workgroup per CU one pair was faster with token-row K (4 x 8192:
+        // 25.04 -> 24.44 us) and is level with the sliced pool (24.06 vs
+        // 24.10).
         if (bpp >= 64 && nwg <= kComputeUnits) go(decode_kernel<128, 4, 1, 1, false, C>, 4);
         else if (bpp >= 64) go(decode_kernel<128, 4, 2, 1, false, C>, 4);
         else go(decode_kernel<128, 3, 2, 1, false, C>, 3);
