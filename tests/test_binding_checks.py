@@ -48,7 +48,6 @@ def test_pool_layout_checked():
     rejects(lambda: pa.write_kv(kn, kn, torch.zeros(B, dtype=torch.int64),
                                 torch.zeros(NB, HKV, 16, D, dtype=BF), vc), "k_cache")
     rejects(lambda: pa.copy_blocks(torch.zeros(NB, HKV, 16, D, dtype=BF), vc, kc, vc), "dst_k")
-    rejects(lambda: pa.copy_blocks(kc, vc, torch.zeros(NB, HKV, 16, D, dtype=BF), vc), "src_k")
 
 
 def test_decode_single_partition_out_shape():
